@@ -1,0 +1,591 @@
+"""Pins for the CPU fp64 oracle (no GPU).
+
+Each check ties the oracle to something other than itself: values worked by
+hand from the pages' stated rules (``tests/golden/``), a pure-Python brute
+force on tiny inputs, torch's CPU SDPA with explicit masks, closed forms, and
+invariants the method must satisfy (block-table permutation, garbage past the
+live prefix, ring vs unrolled storage, GQA vs repeated heads).  The last test
+plants mistakes in the oracle and checks that some pin catches each one.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Test-side construction of storage (independent of the oracle's gathers).
+# ---------------------------------------------------------------------------
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def raw(x: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits(x) if dtype == "bf16" else np.asarray(x, dtype=np.float32)
+
+
+def garbage(shape, dtype, kind="nan", rng=None):
+    if kind == "zero":
+        return raw(np.zeros(shape, np.float32), dtype)
+    if kind == "nan":
+        return raw(np.full(shape, np.nan, np.float32), dtype)
+    if kind == "inf":
+        return raw(np.full(shape, np.inf, np.float32), dtype)
+    g = np.random.default_rng(99)   # its own stream: garbage never shifts the real values
+    return raw(g.standard_normal(shape).astype(np.float32) * 1e4, dtype)
+
+
+def place_paged(pool, table_row, logical):
+    """Put logical keys 0..E-1 into the pool block by block: table entry k
+    names the pool block that holds tokens 16k .. 16k+15."""
+    E = logical.shape[0]
+    nb = (E + 15) // 16
+    for k in range(nb):
+        n = min(16, E - 16 * k)
+        pool[table_row[k], :n] = logical[16 * k:16 * k + n]
+
+
+def place_ring(store, col, logical):
+    """Append logical keys 0..E-1 one at a time into a ring column: each new
+    key goes to the row after the previous one, wrapping at the end."""
+    rows = store.shape[0]
+    r = 0
+    for j in range(logical.shape[0]):
+        store[r, col] = logical[j]
+        r = r + 1 if r + 1 < rows else 0
+
+
+# ---------------------------------------------------------------------------
+# Pure-Python brute force (the definition with nested loops and math.exp).
+# ---------------------------------------------------------------------------
+
+def brute_unit(q, K, V, E, scale, causal, window):
+    """q [L][Hq][D], K/V [E][Hkv][D] logical float lists -> out [L][Hq][D]."""
+    L, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(K[0]) if E else 1
+    G = Hq // Hkv
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(L)]
+    for i in range(L):
+        p = E - L + i
+        vis = []
+        for j in range(E):
+            if causal and j > p:
+                continue
+            if window > 0 and j < p - window + 1:
+                continue
+            vis.append(j)
+        if not vis:
+            continue
+        for h in range(Hq):
+            g = h // G
+            s = [scale * sum(q[i][h][d] * K[j][g][d] for d in range(D)) for j in vis]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            tot = sum(w)
+            out[i][h] = [sum(w[k] * V[vis[k]][g][d] for k in range(len(vis))) / tot
+                         for d in range(D)]
+    return out
+
+
+def f64(a, dtype):
+    """Test-side widening through torch (independent of the oracle's decoder)."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        return t.to(torch.float64).numpy()
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def make_paged_case(rng, *, lengths, q_lens, hq, hkv, d, dtype, num_blocks, max_blocks,
+                    tail="nan", identity=False):
+    """Random logical K/V per sequence placed through a random (or identity) table."""
+    nbs = [(E + 15) // 16 for E in lengths]
+    perm = rng.permutation(num_blocks)
+    if identity:
+        perm = np.arange(num_blocks)
+    table = np.full((len(lengths), max_blocks), 0x7FFFFFFF, dtype=np.int64)
+    k = 0
+    for b, nb in enumerate(nbs):
+        table[b, :nb] = perm[k:k + nb]
+        k += nb
+    pool_k = garbage((num_blocks, 16, hkv, d), dtype, tail, rng)
+    pool_v = garbage((num_blocks, 16, hkv, d), dtype, tail, rng)
+    logical = []
+    for b, E in enumerate(lengths):
+        Kl = raw(rng.standard_normal((E, hkv, d)).astype(np.float32), dtype)
+        Vl = raw(rng.standard_normal((E, hkv, d)).astype(np.float32), dtype)
+        place_paged(pool_k, table[b], Kl)
+        place_paged(pool_v, table[b], Vl)
+        logical.append((Kl, Vl))
+    total_q = sum(q_lens)
+    q = raw(rng.standard_normal((total_q, hq, d)).astype(np.float32), dtype)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    return dict(q=q, k=pool_k, v=pool_v, table=table, cu=cu,
+                used=np.array(lengths, dtype=np.int64), logical=logical)
+
+
+# ---------------------------------------------------------------------------
+# Pins as plain functions (so the mutation test can re-run them).
+# ---------------------------------------------------------------------------
+
+def pin_golden_causal_rule():
+    fx = _load("causal_rule.json")
+    for c in fx["cases"]:
+        E, L = c["start"] + c["T"], c["T"]
+        for i, want in enumerate(c["visible"]):
+            lo, hi = oracle.visible_range(E, L, i, True, 0)
+            assert list(range(lo, hi)) == want, (c, i)
+
+
+def pin_golden_slots():
+    fx = _load("slots.json")
+    bt = fx["paged"]["block_table"]
+    for j, s in fx["paged"]["cases"]:
+        assert oracle.paged_slot(bt, j) == s
+    slots, ok = oracle.gather_slots_paged(np.array(bt), 41, 8)
+    assert ok.all()
+    for j, s in fx["paged"]["cases"]:
+        assert int(slots[j]) == s
+    r = fx["ring"]
+    for pos, col, s in r["cases"]:
+        assert oracle.ring_slot(pos, r["rows"], r["cols"], col) == s
+    for n, s in fx["decode_append"]["cases"]:
+        ident = np.arange((n + 15) // 16 + 1)
+        assert int(oracle.paged_slots_for(ident[None, :], [0], [n - 1])[0]) == s
+
+
+def _golden_column(case, causal, window):
+    q = np.array(case["q"], dtype=np.float32)[:, None, :]
+    k = np.array(case["k"], dtype=np.float32)
+    v = np.array(case["v"], dtype=np.float32)
+    E, L = k.shape[0], q.shape[0]
+    store_k = np.full((16, 1, 1, k.shape[1]), np.nan, np.float32)
+    store_v = np.full((16, 1, 1, k.shape[1]), np.nan, np.float32)
+    store_k[:E, 0, 0] = k
+    store_v[:E, 0, 0] = v
+    info = np.array([[0, L, 0, E]])
+    return oracle.column_attention(q, store_k, store_v, info, dtype="f32", scale=case["scale"],
+                                   causal=causal, window=window)[:, 0, :]
+
+
+def pin_golden_closed_forms():
+    fx = _load("closed_forms.json")
+    c = fx["two_key"]
+    np.testing.assert_allclose(_golden_column(c, False, 0), c["out"], atol=1e-12)
+    c = fx["causal_offset"]
+    np.testing.assert_allclose(_golden_column(c, True, 0), c["out"], atol=1e-12)
+    c = fx["window_two"]
+    np.testing.assert_allclose(_golden_column(c, True, c["window"]), c["out"], atol=1e-12)
+
+
+def pin_window_span():
+    """Ring of window + max_write - 1 rows holds exactly what a causal step sees."""
+    for W in (1, 2, 5, 16):
+        for T in (1, 2, 3, 7):
+            start = 40
+            E = start + T
+            lows, highs = zip(*(oracle.visible_range(E, T, i, True, W) for i in range(T)))
+            assert max(highs) - min(lows) == W + T - 1
+            for i in range(T):
+                lo, hi = oracle.visible_range(E, T, i, True, W)
+                assert hi - lo == W
+
+
+def pin_brute_force(seed=0):
+    rng = np.random.default_rng(seed)
+    for causal in (False, True):
+        for window in (0, 1, 3, 17):
+            for hq, hkv in ((2, 1), (4, 2), (2, 2)):
+                lengths = [int(x) for x in rng.integers(1, 41, size=3)]
+                q_lens = [int(rng.integers(1, min(4, E) + 1)) for E in lengths]
+                d = 4
+                case = make_paged_case(rng, lengths=lengths, q_lens=q_lens, hq=hq, hkv=hkv,
+                                       d=d, dtype="f32", num_blocks=12, max_blocks=4)
+                got = oracle.paged_attention(case["q"], case["k"], case["v"], case["table"],
+                                             case["cu"], case["used"], dtype="f32", scale=0.7,
+                                             causal=causal, window=window)
+                for b, E in enumerate(lengths):
+                    Kl, Vl = case["logical"][b]
+                    qb = case["q"][case["cu"][b]:case["cu"][b + 1]]
+                    ref = brute_unit(qb.astype(np.float64).tolist(), Kl.astype(np.float64).tolist(),
+                                     Vl.astype(np.float64).tolist(), E, 0.7, causal, window)
+                    np.testing.assert_allclose(got[case["cu"][b]:case["cu"][b + 1]], ref,
+                                               atol=1e-12, rtol=0)
+
+
+def pin_brute_force_column(seed=1):
+    rng = np.random.default_rng(seed)
+    rows, cols, hq, hkv, d = 12, 3, 4, 2, 4
+    for causal in (False, True):
+        for window in (0, 2, 5):
+            q_lens = [1, 3, 2]
+            ends = [9, 20, 30] if window else [9, 11, 7]   # ring wraps only under a window
+            ks = garbage((rows, cols, hkv, d), "f32", "nan")
+            vs = garbage((rows, cols, hkv, d), "f32", "nan")
+            logical = []
+            for s, E in enumerate(ends):
+                Kl = rng.standard_normal((E, hkv, d)).astype(np.float32)
+                Vl = rng.standard_normal((E, hkv, d)).astype(np.float32)
+                place_ring(ks, s, Kl)
+                place_ring(vs, s, Vl)
+                logical.append((Kl, Vl))
+            total_q = 10
+            q = rng.standard_normal((total_q, hq, d)).astype(np.float32)
+            info = np.array([[0, 1, 0, ends[0]], [2, 3, 1, ends[1]], [6, 2, 2, ends[2]]])
+            got = oracle.column_attention(q, ks, vs, info, dtype="f32", scale=0.9,
+                                          causal=causal, window=window)
+            covered = set()
+            for s, (q0, L, c, E) in enumerate(info.tolist()):
+                Kl, Vl = logical[s]
+                ref = brute_unit(q[q0:q0 + L].astype(np.float64).tolist(),
+                                 Kl.astype(np.float64).tolist(), Vl.astype(np.float64).tolist(),
+                                 E, 0.9, causal, window)
+                np.testing.assert_allclose(got[q0:q0 + L], ref, atol=1e-12, rtol=0)
+                covered.update(range(q0, q0 + L))
+            for r in range(total_q):
+                if r not in covered:
+                    assert (got[r] == 0).all()
+
+
+def pin_sdpa_noncausal_decode(seed=2):
+    rng = np.random.default_rng(seed)
+    hq, hkv, d, E = 8, 2, 16, 77
+    case = make_paged_case(rng, lengths=[E], q_lens=[1], hq=hq, hkv=hkv, d=d, dtype="bf16",
+                           num_blocks=8, max_blocks=8, identity=True)
+    got = oracle.paged_attention(case["q"], case["k"], case["v"], case["table"], case["cu"],
+                                 case["used"], dtype="bf16", scale=0.25)
+    Kl, Vl = case["logical"][0]
+    qt = torch.from_numpy(f64(case["q"], "bf16")).permute(1, 0, 2)[None]          # [1,Hq,1,D]
+    kt = torch.from_numpy(f64(Kl, "bf16")).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)[None]
+    vt = torch.from_numpy(f64(Vl, "bf16")).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.25)
+    np.testing.assert_allclose(got, ref[0].permute(1, 0, 2).numpy(), atol=1e-12, rtol=0)
+
+
+def pin_sdpa_causal_offset(seed=3):
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = 4, 4, 8
+    for start, T in ((5, 4), (17, 3), (0, 6)):
+        E = start + T
+        case = make_paged_case(rng, lengths=[E], q_lens=[T], hq=hq, hkv=hkv, d=d, dtype="f32",
+                               num_blocks=4, max_blocks=4)
+        got = oracle.paged_attention(case["q"], case["k"], case["v"], case["table"], case["cu"],
+                                     case["used"], dtype="f32", scale=0.5, causal=True)
+        Kl, Vl = case["logical"][0]
+        qt = torch.from_numpy(case["q"].astype(np.float64)).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(Kl.astype(np.float64)).permute(1, 0, 2)[None]
+        vt = torch.from_numpy(Vl.astype(np.float64)).permute(1, 0, 2)[None]
+        q_pos = torch.arange(start, start + T)[:, None]
+        k_pos = torch.arange(E)[None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=k_pos <= q_pos,
+                                                               scale=0.5)
+        np.testing.assert_allclose(got, ref[0].permute(1, 0, 2).numpy(), atol=1e-12, rtol=0)
+        if start > 0 and T > 1:
+            top_left = torch.nn.functional.scaled_dot_product_attention(
+                qt, kt[:, :, :T], vt[:, :, :T], is_causal=True, scale=0.5)
+            assert not np.allclose(got, top_left[0].permute(1, 0, 2).numpy(), atol=1e-6)
+
+
+def pin_window1_gather(seed=4):
+    """Causal window 1 with q_len = E: row i sees only key i, so out[i] is V[i] exactly."""
+    rng = np.random.default_rng(seed)
+    for dtype in ("bf16", "f32"):
+        E = 45
+        case = make_paged_case(rng, lengths=[E, 20], q_lens=[E, 20], hq=4, hkv=2, d=8,
+                               dtype=dtype, num_blocks=12, max_blocks=4)
+        got = oracle.paged_attention(case["q"], case["k"], case["v"], case["table"], case["cu"],
+                                     case["used"], dtype=dtype, scale=1.3, causal=True, window=1)
+        for b in range(2):
+            Vl = f64(case["logical"][b][1], dtype)
+            o = got[case["cu"][b]:case["cu"][b + 1]]
+            for h in range(4):
+                assert np.array_equal(o[:, h, :], Vl[:, h // 2, :])
+    # the same through a wrapped ring column
+    rows, E = 16, 50
+    ks = garbage((rows, 2, 1, 4), "f32")
+    vs = garbage((rows, 2, 1, 4), "f32")
+    Vl = rng.standard_normal((E, 1, 4)).astype(np.float32)
+    place_ring(ks, 1, rng.standard_normal((E, 1, 4)).astype(np.float32))
+    place_ring(vs, 1, Vl)
+    L = 16
+    q = rng.standard_normal((L, 1, 4)).astype(np.float32)
+    got = oracle.column_attention(q, ks, vs, np.array([[0, L, 1, E]]), dtype="f32", scale=1.0,
+                                  causal=True, window=1)
+    assert np.array_equal(got[:, 0, :], Vl[E - L:, 0, :].astype(np.float64))
+
+
+def pin_single_key(seed=5):
+    rng = np.random.default_rng(seed)
+    case = make_paged_case(rng, lengths=[1, 1], q_lens=[1, 1], hq=4, hkv=1, d=8, dtype="bf16",
+                           num_blocks=6, max_blocks=2)
+    got = oracle.paged_attention(case["q"], case["k"], case["v"], case["table"], case["cu"],
+                                 case["used"], dtype="bf16", scale=10.0)
+    for b in range(2):
+        Vl = f64(case["logical"][b][1], "bf16")
+        for h in range(4):
+            assert np.array_equal(got[b, h], Vl[0, 0])
+
+
+def pin_permutation_invariance(seed=6):
+    rng = np.random.default_rng(seed)
+    lengths = [37, 5, 64]
+    a = make_paged_case(np.random.default_rng(seed), lengths=lengths, q_lens=[1, 2, 3], hq=4,
+                        hkv=2, d=8, dtype="bf16", num_blocks=10, max_blocks=4, identity=True)
+    b = make_paged_case(np.random.default_rng(seed), lengths=lengths, q_lens=[1, 2, 3], hq=4,
+                        hkv=2, d=8, dtype="bf16", num_blocks=10, max_blocks=4)
+    for causal in (False, True):
+        ra = oracle.paged_attention(a["q"], a["k"], a["v"], a["table"], a["cu"], a["used"],
+                                    dtype="bf16", scale=0.4, causal=causal, window=9)
+        rb = oracle.paged_attention(b["q"], b["k"], b["v"], b["table"], b["cu"], b["used"],
+                                    dtype="bf16", scale=0.4, causal=causal, window=9)
+        assert np.array_equal(ra, rb)
+    del rng
+
+
+def pin_garbage_invariance(seed=7):
+    outs = []
+    for kind in ("zero", "nan", "inf", "big"):
+        c = make_paged_case(np.random.default_rng(seed), lengths=[23, 40], q_lens=[2, 1], hq=2,
+                            hkv=1, d=4, dtype="bf16", num_blocks=9, max_blocks=5, tail=kind)
+        if kind == "nan":
+            c["table"][0, 2:] = -1
+        outs.append(oracle.paged_attention(c["q"], c["k"], c["v"], c["table"], c["cu"],
+                                           c["used"], dtype="bf16", scale=0.5, causal=True))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert np.isfinite(outs[0]).all()
+
+
+def pin_uncovered_rows_zero(seed=8):
+    rng = np.random.default_rng(seed)
+    c = make_paged_case(rng, lengths=[30], q_lens=[2], hq=2, hkv=1, d=4, dtype="f32",
+                        num_blocks=3, max_blocks=2)
+    q = np.concatenate([c["q"], raw(rng.standard_normal((3, 2, 4)), "f32")])
+    got = oracle.paged_attention(q, c["k"], c["v"], c["table"], c["cu"], c["used"], dtype="f32",
+                                 scale=1.0)
+    assert (got[2:] == 0).all() and (got[:2] != 0).any()
+    # q_len beyond the static bound: rows past it are uncovered
+    got2 = oracle.paged_attention(c["q"], c["k"], c["v"], c["table"], c["cu"], c["used"],
+                                  dtype="f32", scale=1.0, max_seqlen_q=1)
+    assert (got2[1] == 0).all() and np.array_equal(got2[0], got[0])
+    # empty sequence, causal row before the first key
+    got3 = oracle.paged_attention(c["q"], c["k"], c["v"], c["table"], c["cu"],
+                                  np.array([0]), dtype="f32", scale=1.0)
+    assert (got3 == 0).all()
+    got4 = oracle.paged_attention(c["q"], c["k"], c["v"], c["table"], c["cu"],
+                                  np.array([1]), dtype="f32", scale=1.0, causal=True)
+    assert (got4[0] == 0).all() and (got4[1] != 0).any()
+
+
+def pin_window_large_is_none(seed=9):
+    c = make_paged_case(np.random.default_rng(seed), lengths=[50, 7], q_lens=[5, 3], hq=4, hkv=2,
+                        d=8, dtype="bf16", num_blocks=8, max_blocks=4)
+    for causal in (False, True):
+        a = oracle.paged_attention(c["q"], c["k"], c["v"], c["table"], c["cu"], c["used"],
+                                   dtype="bf16", scale=0.3, causal=causal)
+        b = oracle.paged_attention(c["q"], c["k"], c["v"], c["table"], c["cu"], c["used"],
+                                   dtype="bf16", scale=0.3, causal=causal, window=55)
+        assert np.array_equal(a, b)
+
+
+def pin_ring_equals_unrolled(seed=10):
+    rng = np.random.default_rng(seed)
+    rows, E, L, W = 10, 37, 3, 6
+    Kl = rng.standard_normal((E, 2, 4)).astype(np.float32)
+    Vl = rng.standard_normal((E, 2, 4)).astype(np.float32)
+    ring_k = garbage((rows, 1, 2, 4), "f32")
+    ring_v = garbage((rows, 1, 2, 4), "f32")
+    place_ring(ring_k, 0, Kl)
+    place_ring(ring_v, 0, Vl)
+    flat_k = garbage((64, 1, 2, 4), "f32")
+    flat_v = garbage((64, 1, 2, 4), "f32")
+    flat_k[:E, 0] = Kl
+    flat_v[:E, 0] = Vl
+    q = rng.standard_normal((L, 4, 4)).astype(np.float32)
+    info = np.array([[0, L, 0, E]])
+    a = oracle.column_attention(q, ring_k, ring_v, info, dtype="f32", scale=0.6, causal=True,
+                                window=W)
+    b = oracle.column_attention(q, flat_k, flat_v, info, dtype="f32", scale=0.6, causal=True,
+                                window=W)
+    assert np.array_equal(a, b)
+
+
+def pin_gqa_repeat(seed=11):
+    rng = np.random.default_rng(seed)
+    c = make_paged_case(rng, lengths=[33], q_lens=[2], hq=6, hkv=2, d=8, dtype="f32",
+                        num_blocks=3, max_blocks=3)
+    a = oracle.paged_attention(c["q"], c["k"], c["v"], c["table"], c["cu"], c["used"],
+                               dtype="f32", scale=0.5, causal=True)
+    kr = np.repeat(c["k"], 3, axis=2)
+    vr = np.repeat(c["v"], 3, axis=2)
+    b = oracle.paged_attention(c["q"], kr, vr, c["table"], c["cu"], c["used"], dtype="f32",
+                               scale=0.5, causal=True)
+    np.testing.assert_allclose(a, b, atol=1e-12, rtol=0)
+
+
+def pin_closed_form_means(seed=12):
+    rng = np.random.default_rng(seed)
+    c = make_paged_case(rng, lengths=[29], q_lens=[1], hq=2, hkv=1, d=4, dtype="f32",
+                        num_blocks=2, max_blocks=2, identity=True)
+    # constant V -> that constant
+    v = c["v"].copy()
+    v[:, :, :, :] = np.float32(0.375)
+    o = oracle.paged_attention(c["q"], c["k"], v, c["table"], c["cu"], c["used"], dtype="f32",
+                               scale=2.0)
+    np.testing.assert_allclose(o, 0.375, atol=1e-15, rtol=0)
+    # q = 0 -> mean of visible V
+    q0 = np.zeros_like(c["q"])
+    o = oracle.paged_attention(q0, c["k"], c["v"], c["table"], c["cu"], c["used"], dtype="f32",
+                               scale=2.0)
+    mean = c["logical"][0][1].astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(o[0, 0], mean[0], atol=1e-12, rtol=0)
+    # all keys equal -> mean of visible V
+    k = c["k"].copy()
+    k[:, :, :, :] = np.float32(-1.25)
+    o = oracle.paged_attention(c["q"], k, c["v"], c["table"], c["cu"], c["used"], dtype="f32",
+                               scale=2.0)
+    np.testing.assert_allclose(o[0, 1], mean[0], atol=1e-12, rtol=0)
+
+
+def pin_kv_append_bits():
+    n, h, d = 6, 2, 3
+    k = np.arange(n * h * d, dtype=np.uint16).reshape(n, h, d)
+    v = (np.arange(n * h * d, dtype=np.uint16) + 1000).reshape(n, h, d)
+    specials = np.array([0x7FC1, 0xFFFF, 0x7F81, 0x8000, 0x0001, 0xFF80], dtype=np.uint16)
+    kn = np.stack([specials.reshape(h, d), specials[::-1].reshape(h, d), specials.reshape(h, d)])
+    vn = kn[::-1].copy()
+    ko, vo = oracle.kv_append(k, v, kn, vn, [4, -1, 6])
+    assert np.array_equal(ko[4], kn[0]) and np.array_equal(vo[4], vn[0])
+    untouched = [0, 1, 2, 3, 5]
+    assert np.array_equal(ko[untouched], k[untouched]) and np.array_equal(vo[untouched], v[untouched])
+    k32 = np.zeros((3, 1, 2), dtype=np.uint32)
+    kn32 = np.array([[[0x7FA00001, 0xFFC00000]]], dtype=np.uint32)
+    ko32, _ = oracle.kv_append(k32, k32, kn32, kn32, [2])
+    assert ko32[2, 0, 0] == 0x7FA00001 and ko32[2, 0, 1] == 0xFFC00000
+
+
+def pin_bf16_decode():
+    """bfloat16 bit patterns with known values (IEEE binary32 upper halves)."""
+    known = {0x3F80: 1.0, 0xC000: -2.0, 0x3FC0: 1.5, 0x0000: 0.0, 0x4049: 3.140625,
+             0x7F80: np.inf, 0xFF80: -np.inf, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126}
+    bits = np.array(list(known), dtype=np.uint16)
+    got = oracle.bf16_bits_to_f64(bits)
+    assert np.array_equal(got, np.array(list(known.values())))
+    assert np.isnan(oracle.bf16_bits_to_f64(np.array([0x7FC0, 0xFFC1], dtype=np.uint16))).all()
+    rnd = np.random.default_rng(13).integers(0, 0x7F80, size=4096).astype(np.uint16)
+    assert np.array_equal(oracle.to_f64(rnd, "bf16"), f64(rnd, "bf16"))
+
+
+ALL_PINS = [
+    pin_bf16_decode,
+    pin_golden_causal_rule, pin_golden_slots, pin_golden_closed_forms, pin_window_span,
+    pin_brute_force, pin_brute_force_column, pin_sdpa_noncausal_decode, pin_sdpa_causal_offset,
+    pin_window1_gather, pin_single_key, pin_permutation_invariance, pin_garbage_invariance,
+    pin_uncovered_rows_zero, pin_window_large_is_none, pin_ring_equals_unrolled, pin_gqa_repeat,
+    pin_closed_form_means, pin_kv_append_bits,
+]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_oracle_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each must make at least one pin fail.
+# ---------------------------------------------------------------------------
+
+def _top_left_causal(E, L, i, causal, window):
+    p = i
+    hi = min(E, p + 1) if causal else E
+    lo = max(0, p - window + 1) if window > 0 else 0
+    return lo, max(lo, hi)
+
+
+def _window_off_by_one(E, L, i, causal, window):
+    p = E - L + i
+    hi = min(E, p + 1) if causal else E
+    lo = max(0, p - window) if window > 0 else 0
+    return lo, max(lo, hi)
+
+
+def _causal_excludes_self(E, L, i, causal, window):
+    p = E - L + i
+    hi = min(E, p) if causal else E
+    lo = max(0, p - window + 1) if window > 0 else 0
+    return lo, max(lo, hi)
+
+
+_real_gather = oracle.gather_slots_paged
+
+
+def _gather_transposed(row, E, nb):
+    slots, ok = _real_gather(row, E, nb)
+    jj = np.arange(E)
+    blk = np.asarray(row).astype(np.int64)[jj // 16]
+    return np.where(ok, blk * 16 + (15 - jj % 16), 0), ok
+
+
+def _gather_no_table(row, E, nb):
+    jj = np.arange(E)
+    return jj.astype(np.int64), np.ones(E, dtype=bool)
+
+
+_real_attend = oracle.attend_unit
+
+
+def _attend_no_scale(q, keys, vals, ok, E, scale, causal, window, chunk=64):
+    return _real_attend(q, keys, vals, ok, E, 1.0, causal, window, chunk)
+
+
+def _attend_swapped_kv(q, keys, vals, ok, E, scale, causal, window, chunk=64):
+    return _real_attend(q, vals, keys, ok, E, scale, causal, window, chunk)
+
+
+def _attend_last_kv_head(q, keys, vals, ok, E, scale, causal, window, chunk=64):
+    return _real_attend(q, keys[:, ::-1], vals[:, ::-1], ok, E, scale, causal, window, chunk)
+
+
+_real_ring = oracle.ring_slot
+
+
+MUTANTS = [
+    ("visible_range", _top_left_causal),
+    ("visible_range", _window_off_by_one),
+    ("visible_range", _causal_excludes_self),
+    ("gather_slots_paged", _gather_transposed),
+    ("gather_slots_paged", _gather_no_table),
+    ("attend_unit", _attend_no_scale),
+    ("attend_unit", _attend_swapped_kv),
+    ("attend_unit", _attend_last_kv_head),
+    ("ring_slot", lambda p, rows, cols, col: (p % rows) + col * rows),
+    ("bf16_bits_to_f64", lambda b: (np.asarray(b).astype(np.uint32) << 15).view(np.float32)
+     .astype(np.float64)),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[f"{n}-{i}" for i, (n, _) in enumerate(MUTANTS)])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant):
+    monkeypatch.setattr(oracle, name, mutant)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake in {name}"
