@@ -1,0 +1,194 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: K/V append and varlen decode attention
+ * over a paged KV cache or a column-packed ring store, for AMD gfx950.
+ *
+ * Sources of the operations (pages, by title and section):
+ *  - vLLM-Omni "paged_decode" (SenseNova-U1), PagedDecodeCache class docstring
+ *    and PagedDecodeCache.attend: per-layer K/V laid out
+ *    (num_blocks, BLOCK_SIZE = 16, kv_heads, head_dim), read through a block
+ *    table; the live length (seqused_k) and the write slot live in device
+ *    tensors so one captured graph serves every length in a bucket; append this
+ *    step's K/V, then attend over the whole valid prefix with
+ *    flash_attn_varlen_func(max_seqlen_q, cu_seqlens_q, max_seqlen_k,
+ *    seqused_k, block_table, softmax_scale, causal).
+ *  - ExecuTorch PR #24073 "Add a batched-sequence CUDA KV cache" (the
+ *    sdpa_varlen and lowering parts): a [rows, cols, H, D] column store, a device
+ *    segment table seq_info Int32[S, 4] = (q_start, q_len, col, kv_end), causal
+ *    and non-causal, sliding window over ring storage, GQA, rows no segment
+ *    covers zeroed, split-K for short steps; in-graph writes to slot
+ *    (position % rows) * columns + column.
+ *  - tiny-llm kv_cache.py, causal_kwargs: with T new queries over start + T
+ *    keys, query i sees keys 0 .. start + i.
+ *
+ * Conventions for every call:
+ *  - All pointers are DEVICE pointers unless stated.  The caller owns every
+ *    buffer; the library never allocates, frees, synchronises or reads device
+ *    memory from the host, and keeps no pointer after a call returns.  Work is
+ *    enqueued on `stream` (a hipStream_t; NULL is the default stream), so every
+ *    call may be captured into a hipGraph.  The launch geometry depends only on
+ *    host arguments: lengths, tables and slots are read on the device.
+ *  - Tensors are dense and row-major.  q, K, V, k_new, v_new and out share one
+ *    element type (`dtype`); accumulation is fp32; out is rounded to nearest-even.
+ *  - Host-checkable argument errors return before anything is enqueued:
+ *    PKV_EINVAL (null pointer, non-positive size, q_heads % kv_heads != 0,
+ *    head_dim % 8 != 0 or head_dim > 256, block_size != 16, both or neither
+ *    addressing mode, num_segments > 2 * cols, a window with ring storage that
+ *    cannot hold window + max_seqlen_q - 1 rows), PKV_EUNSUPPORTED (a head_dim
+ *    or group size with no compiled kernel), PKV_EWORKSPACE (workspace too
+ *    small).  PKV_EHIP reports a failed launch.  pkv_last_error() gives text.
+ *  - Device-side values follow fixed rules instead of being checked:
+ *      E = clamp(seqused_k[b], 0, min(max_seqlen_k, 16 * max_blocks_per_seq));
+ *      column-mode kv_end below 0 counts as 0;
+ *      row i of a unit with L query rows sits at position p = E - L + i and
+ *      sees keys j with j < E, (causal: j <= p), (window > 0: j >= p - window + 1);
+ *      a live key whose block-table entry is outside [0, num_blocks), or a
+ *      segment whose column is outside [0, cols), contributes no keys;
+ *      a row with no visible key is 0, and so is every row of [0, total_q)
+ *      that no unit covers (rows of a unit past max_seqlen_q count as uncovered);
+ *      only the live keys a unit can see are read: storage past seqused_k and
+ *      block-table entries past ceil(E / 16) are never dereferenced.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_EINVAL = 1,
+    PKV_EUNSUPPORTED = 2,
+    PKV_EWORKSPACE = 3,
+    PKV_EHIP = 4
+} pkv_status;
+
+typedef enum pkv_dtype {
+    PKV_F32 = 0,
+    PKV_BF16 = 1
+} pkv_dtype;
+
+#define PKV_BLOCK_SIZE 16
+
+/*
+ * pkv_kv_append -- write new K/V rows into slots of a flat cache view.
+ * (vLLM-Omni paged_decode, PagedDecodeCache.attend: index_copy of this step's
+ * K and V at the slot held in a device tensor; ExecuTorch PR #24073: in-graph
+ * write to (position % rows) * columns + column.)
+ *
+ * k_cache, v_cache : [num_slots, kv_heads, head_dim], written in place.  A paged
+ *                    cache [num_blocks, 16, kv_heads, head_dim] is the flat view
+ *                    with num_slots = 16 * num_blocks; a column store
+ *                    [rows, cols, kv_heads, head_dim] has num_slots = rows * cols.
+ * k_new, v_new     : [num_tokens, kv_heads, head_dim], read only.
+ * slot_mapping     : int64 [num_tokens]; token t goes to slot slot_mapping[t].
+ *                    A slot outside [0, num_slots) is skipped.  Two tokens with
+ *                    the same slot leave that slot undefined.
+ * The copy moves raw 16/32-bit words: every bit pattern (NaN payloads included)
+ * arrives unchanged.  num_tokens == 0 enqueues nothing and returns PKV_OK.
+ */
+pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
+                         const void* k_new, const void* v_new, int32_t num_tokens,
+                         const int64_t* slot_mapping, int32_t kv_heads, int32_t head_dim,
+                         pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_paged_decode_attn -- one query token per sequence over a paged cache.
+ * (vLLM-Omni paged_decode, PagedDecodeCache.attend with max_seqlen_q = 1,
+ * cu_seqlens_q = [0, 1, ..], max_seqlen_k = bucket, causal = False.)
+ *
+ * out, q       : [num_seqs, q_heads, head_dim]; row b is sequence b's query.
+ * k_cache, v_cache : [num_blocks, 16, kv_heads, head_dim].
+ * block_table  : int32 [num_seqs, max_blocks_per_seq]; entry k names the pool
+ *                block that holds tokens 16k .. 16k + 15 of the sequence.
+ * seqused_k    : int32 [num_seqs], live keys per sequence, this step's included.
+ * max_seqlen_k : host bound on seqused_k (the bucket).
+ * k_new, v_new : optional [num_seqs, kv_heads, head_dim].  When both are given,
+ *                the call first appends them at position seqused_k[b] - 1 of
+ *                each sequence (the slot found through block_table) and then
+ *                attends, as one step.  When NULL the cache is only read.
+ * softmax_scale: multiplies q.k before the softmax.
+ * causal       : with one query per sequence causal equals non-causal.
+ * window       : > 0 keeps the last `window` keys (p - window + 1 .. p).
+ * num_splits   : split-K partitions per (sequence, kv head); 0 lets the library
+ *                pick from the host arguments.  Results of different split counts
+ *                agree to rounding; a fixed split count is deterministic.
+ * workspace    : device scratch of at least pkv_attn_workspace_bytes(num_seqs, 1,
+ *                max_seqlen_k, q_heads, kv_heads, head_dim, num_splits) bytes
+ *                (may be NULL when that is 0).  Its contents need no initialisation.
+ */
+pkv_status pkv_paged_decode_attn(void* out, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 int32_t num_blocks, int32_t block_size,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* seqused_k, int32_t num_seqs, int32_t max_seqlen_k,
+                                 const void* k_new, const void* v_new,
+                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                 float softmax_scale, int32_t causal, int32_t window,
+                                 int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                 pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_varlen_attn -- packed query rows over a paged cache or a column store.
+ * Exactly one of {block_table, seq_info} is non-NULL.
+ *
+ * out, q       : [total_q, q_heads, head_dim].
+ * k, v         : paged mode [num_blocks, 16, kv_heads, head_dim];
+ *                column mode [rows, cols, kv_heads, head_dim], key j of a
+ *                segment in store row j % rows of its column.
+ * Paged mode   : cu_seqlens_q int32 [num_seqs + 1] (sequence b owns rows
+ *                cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1), seqused_k int32
+ *                [num_seqs], block_table int32 [num_seqs, max_blocks_per_seq].
+ * Column mode  : seq_info int32 [num_segments, 4] = (q_start, q_len, col, kv_end);
+ *                num_segments <= 2 * cols.  Segments must not overlap in rows.
+ *                With a window, rows must be >= window + max_seqlen_q - 1 (the
+ *                ring then holds every key a step can see); without one, the
+ *                caller keeps kv_end <= rows.
+ * max_seqlen_q : host bound on any unit's query rows.
+ * max_seqlen_k : host bound on the keys a unit sees.  Paged mode clamps
+ *                seqused_k to it.  Column mode uses it only to choose the split
+ *                count and requires it > 0 (e.g. window + max_seqlen_q - 1, or rows).
+ * Other arguments as for pkv_paged_decode_attn.  workspace must hold
+ * pkv_attn_workspace_bytes(units, max_seqlen_q, ...) bytes with units =
+ * num_seqs or num_segments.
+ */
+pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q,
+                           const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* seqused_k, int32_t num_seqs,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t block_size,
+                           const int32_t* seq_info, int32_t num_segments, int32_t rows, int32_t cols,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                           float softmax_scale, int32_t causal, int32_t window,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes,
+                           pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_attn_workspace_bytes -- device scratch an attention call with these host
+ * arguments needs (split-K partials); 0 when it needs none.  `units` is num_seqs
+ * (paged) or num_segments (column); num_splits as passed to the call.
+ */
+size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                int32_t num_splits);
+
+/* Split count the library uses for these host arguments (num_splits = 0 picks). */
+int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                            int32_t num_splits);
+
+/* Static text for a status code. */
+const char* pkv_status_string(pkv_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

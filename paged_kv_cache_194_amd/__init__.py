@@ -1,0 +1,237 @@
+"""Python binding of libpagedkv.so: argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, checks that
+their dtypes, shapes and contiguity match what the C ABI expects, and calls the
+entry point of the same name on the current HIP stream.  All computation runs
+in the library's HIP kernels; if the library is missing this module raises
+instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PagedKVError", "BLOCK_SIZE", "lib", "library_path", "kv_append", "paged_decode_attn",
+    "varlen_attn", "attn_workspace_bytes", "attn_num_splits", "status_string", "last_error",
+    "EXPORTED_SYMBOLS",
+]
+
+BLOCK_SIZE = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+EXPORTED_SYMBOLS = (
+    "pkv_kv_append", "pkv_paged_decode_attn", "pkv_varlen_attn", "pkv_attn_workspace_bytes",
+    "pkv_attn_num_splits", "pkv_status_string", "pkv_last_error",
+)
+
+
+class PagedKVError(ValueError):
+    """A non-OK status from libpagedkv.so."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+def _status_name(s: int) -> str:
+    return {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE",
+            4: "PKV_EHIP"}.get(s, f"status {s}")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "pkv_kv_append": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _vp]),
+    "pkv_paged_decode_attn": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
+                                     _vp, _vp, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz,
+                                     _i32, _vp]),
+    "pkv_varlen_attn": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                               _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                               _i32, _i32, _vp, _sz, _i32, _vp]),
+    "pkv_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_attn_num_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        handle = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def status_string(s: int) -> str:
+    return lib().pkv_status_string(s).decode()
+
+
+def last_error() -> str:
+    return lib().pkv_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != PKV_OK:
+        raise PagedKVError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise PagedKVError(PKV_EINVAL, f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise PagedKVError(PKV_EINVAL, msg)
+
+
+def _dev(*ts) -> None:
+    for t in ts:
+        if t is not None:
+            _need(t.is_cuda, "tensors must be on the GPU")
+            _need(t.is_contiguous(), "tensors must be contiguous")
+
+
+def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Write ``k_new``/``v_new`` ``[T, Hkv, D]`` into the flat slot view of the caches."""
+    _dev(k_cache, v_cache, k_new, v_new, slot_mapping)
+    _need(k_new.dim() == 3 and k_new.shape == v_new.shape, "k_new/v_new must be [T, Hkv, D]")
+    _need(k_cache.shape == v_cache.shape, "k_cache and v_cache differ in shape")
+    _need(k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype, "dtypes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == k_new.shape[0],
+          "slot_mapping must be int64 [T]")
+    T, H, D = k_new.shape
+    _need(tuple(k_cache.shape[-2:]) == (H, D), "cache trailing dims must be (Hkv, D)")
+    num_slots = k_cache.numel() // (H * D)
+    _check(lib().pkv_kv_append(_ptr(k_cache), _ptr(v_cache), num_slots, _ptr(k_new), _ptr(v_new),
+                               T, _ptr(slot_mapping), H, D, _dtype(k_new), _stream(k_new)))
+
+
+def attn_workspace_bytes(units: int, max_seqlen_q: int, max_seqlen_k: int, q_heads: int,
+                         kv_heads: int, head_dim: int, num_splits: int = 0) -> int:
+    return int(lib().pkv_attn_workspace_bytes(units, max_seqlen_q, max_seqlen_k, q_heads,
+                                              kv_heads, head_dim, num_splits))
+
+
+def attn_num_splits(units: int, max_seqlen_q: int, max_seqlen_k: int, q_heads: int,
+                    kv_heads: int, head_dim: int, num_splits: int = 0) -> int:
+    return int(lib().pkv_attn_num_splits(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads,
+                                         head_dim, num_splits))
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, like: torch.Tensor):
+    if need == 0:
+        return ws, 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=like.device)
+    _dev(ws)
+    return ws, ws.numel() * ws.element_size()
+
+
+def paged_decode_attn(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_table: torch.Tensor, seqused_k: torch.Tensor,
+                      max_seqlen_k: int, softmax_scale: Optional[float] = None,
+                      causal: bool = False, window: int = 0, num_splits: int = 0,
+                      workspace: Optional[torch.Tensor] = None,
+                      k_new: Optional[torch.Tensor] = None,
+                      v_new: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One query per sequence: ``q``/``out`` ``[B, Hq, D]`` over ``[NB, 16, Hkv, D]`` caches.
+    With ``k_new``/``v_new`` ``[B, Hkv, D]`` the token is appended at position
+    ``seqused_k[b] - 1`` first."""
+    _dev(out, q, k_cache, v_cache, block_table, seqused_k, k_new, v_new)
+    _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, Hq, D]")
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "caches must be [NB, 16, Hkv, D]")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [B, W]")
+    _need(seqused_k.dtype == torch.int32, "seqused_k must be int32")
+    B, Hq, D = q.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    _need(Dk == D and block_table.shape[0] == B and seqused_k.numel() == B, "shape mismatch")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype == out.dtype, "dtypes differ")
+    if k_new is not None or v_new is not None:
+        _need(k_new is not None and v_new is not None, "give both k_new and v_new")
+        _need(tuple(k_new.shape) == (B, Hkv, D) and k_new.shape == v_new.shape, "k_new/v_new must be [B, Hkv, D]")
+        _need(k_new.dtype == v_new.dtype == q.dtype, "dtypes differ")
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    need = attn_workspace_bytes(B, 1, max_seqlen_k, Hq, Hkv, D, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q)
+    _check(lib().pkv_paged_decode_attn(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), NB, BS, _ptr(block_table),
+        block_table.shape[1], _ptr(seqused_k), B, int(max_seqlen_k), _ptr(k_new), _ptr(v_new),
+        Hq, Hkv, D, scale, int(bool(causal)), int(window), int(num_splits), _ptr(workspace),
+        ws_bytes, _dtype(q), _stream(q)))
+    return out
+
+
+def varlen_attn(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                max_seqlen_q: int, max_seqlen_k: int,
+                cu_seqlens_q: Optional[torch.Tensor] = None,
+                seqused_k: Optional[torch.Tensor] = None,
+                block_table: Optional[torch.Tensor] = None,
+                seq_info: Optional[torch.Tensor] = None,
+                softmax_scale: Optional[float] = None, causal: bool = False, window: int = 0,
+                num_splits: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed rows ``q``/``out`` ``[total_q, Hq, D]`` over a paged cache
+    (``cu_seqlens_q``, ``seqused_k``, ``block_table``; ``k``/``v`` ``[NB, 16, Hkv, D]``)
+    or a column store (``seq_info`` ``[S, 4]``; ``k``/``v`` ``[rows, cols, Hkv, D]``)."""
+    _dev(out, q, k, v, cu_seqlens_q, seqused_k, block_table, seq_info)
+    _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [total_q, Hq, D]")
+    _need(k.dim() == 4 and k.shape == v.shape, "k/v must be 4-d and equal in shape")
+    _need(q.dtype == k.dtype == v.dtype == out.dtype, "dtypes differ")
+    total_q, Hq, D = q.shape
+    _need(k.shape[3] == D, "head_dim mismatch")
+    Hkv = k.shape[2]
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    nb = bs = mb = rows = cols = 0
+    num_seqs = num_segments = 0
+    if block_table is not None:
+        _need(seq_info is None, "give block_table or seq_info, not both")
+        _need(cu_seqlens_q is not None and seqused_k is not None, "paged mode needs cu_seqlens_q and seqused_k")
+        _need(block_table.dtype == cu_seqlens_q.dtype == seqused_k.dtype == torch.int32, "index tensors must be int32")
+        num_seqs = seqused_k.numel()
+        _need(cu_seqlens_q.numel() == num_seqs + 1 and block_table.shape[0] == num_seqs, "shape mismatch")
+        nb, bs = k.shape[0], k.shape[1]
+        mb = block_table.shape[1]
+        units = num_seqs
+    else:
+        _need(seq_info is not None, "give block_table or seq_info")
+        _need(seq_info.dtype == torch.int32 and seq_info.dim() == 2 and seq_info.shape[1] == 4,
+              "seq_info must be int32 [S, 4]")
+        num_segments = seq_info.shape[0]
+        rows, cols = k.shape[0], k.shape[1]
+        units = num_segments
+    need = attn_workspace_bytes(units, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q)
+    _check(lib().pkv_varlen_attn(
+        _ptr(out), _ptr(q), total_q, _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(seqused_k),
+        num_seqs, _ptr(block_table), mb, nb, bs, _ptr(seq_info), num_segments, rows, cols,
+        int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, scale, int(bool(causal)), int(window),
+        int(num_splits), _ptr(workspace), ws_bytes, _dtype(q), _stream(q)))
+    return out

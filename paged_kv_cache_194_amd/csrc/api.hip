@@ -1,0 +1,301 @@
+// C ABI of libpagedkv.so: host-side argument checks, split choice, launches.
+// Nothing here allocates, synchronises or reads device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pkv_status ok() {
+    g_last_error[0] = '\0';
+    return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return PKV_OK;
+    return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int32_t kMaxSplits = 256;
+constexpr int32_t kMaxUnits = 65535;
+constexpr int32_t kVecMaxGroup = 8;
+
+int32_t elem_bytes(pkv_dtype d) { return d == PKV_BF16 ? 2 : 4; }
+
+bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
+
+// Shared checks on the head geometry.
+pkv_status check_heads(int32_t q_heads, int32_t kv_heads, int32_t head_dim, pkv_dtype dtype) {
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "unknown dtype %d", (int)dtype);
+    if (q_heads <= 0 || kv_heads <= 0) return fail(PKV_EINVAL, "q_heads and kv_heads must be > 0");
+    if (q_heads % kv_heads != 0)
+        return fail(PKV_EINVAL, "q_heads (%d) is not a multiple of kv_heads (%d)", q_heads, kv_heads);
+    if (head_dim <= 0 || head_dim % 8 != 0 || head_dim > 256)
+        return fail(PKV_EINVAL, "head_dim %d: must be a positive multiple of 8, at most 256", head_dim);
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d has no compiled kernel (64, 128, 256)", head_dim);
+    return PKV_OK;
+}
+
+int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_splits) {
+    if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
+    const int64_t base = (int64_t)(units > 0 ? units : 1) * kv_heads;
+    const int64_t blocks = ((int64_t)(keys > 0 ? keys : 1) + 15) / 16;
+    int64_t s = (2048 + base - 1) / base;        // about 2048 work groups
+    const int64_t cap = blocks / 4 > 0 ? blocks / 4 : 1;   // >= 4 blocks (1 per wave) each
+    if (s > cap) s = cap;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int32_t)(s < 1 ? 1 : s);
+}
+
+size_t vec_workspace(int32_t units, int32_t kv_heads, int32_t group, int32_t head_dim,
+                     int32_t splits) {
+    if (splits <= 1 || group > kVecMaxGroup) return 0;
+    const size_t gt = (size_t)pkv::vec_group_rows(group);
+    return (size_t)units * kv_heads * splits * gt * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+struct Plan {
+    int32_t splits;
+    size_t ws_bytes;
+};
+
+Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_heads, int32_t kv_heads,
+               int32_t head_dim, int32_t num_splits) {
+    Plan pl;
+    pl.splits = pick_splits(units, kv_heads, keys, num_splits);
+    pl.ws_bytes = vec_workspace(units, kv_heads, q_heads / kv_heads, head_dim, pl.splits);
+    (void)max_seqlen_q;
+    return pl;
+}
+
+// Enqueue the attention kernels for a fully checked parameter block.
+pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, const Plan& pl,
+                         void* workspace, hipStream_t stream) {
+    p.num_splits = pl.splits;
+    p.ws_o = nullptr;
+    p.ws_ml = nullptr;
+    if (pl.splits > 1) {
+        const size_t gt = (size_t)pkv::vec_group_rows(p.group);
+        const size_t n = (size_t)p.num_units * p.kv_heads * pl.splits * gt;
+        p.ws_o = (float*)workspace;
+        p.ws_ml = p.ws_o + n * head_dim;
+    }
+    if (p.num_units == 0 && p.total_q == 0) return ok();
+    if (p.mode != pkv::kPagedDecode) {
+        pkv_status s = hip_status(pkv::launch_zero_uncovered(p, dtype, head_dim, stream), "zero rows");
+        if (s != PKV_OK) return s;
+    }
+    if (p.num_units > 0) {
+        pkv_status s = hip_status(pkv::launch_attn_vec(p, dtype, head_dim, stream), "attention");
+        if (s != PKV_OK) return s;
+        if (pl.splits > 1) {
+            s = hip_status(pkv::launch_attn_vec_combine(p, dtype, head_dim, stream), "combine");
+            if (s != PKV_OK) return s;
+        }
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+    switch (s) {
+        case PKV_OK: return "ok";
+        case PKV_EINVAL: return "invalid argument";
+        case PKV_EUNSUPPORTED: return "unsupported configuration";
+        case PKV_EWORKSPACE: return "workspace too small";
+        case PKV_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_last_error; }
+
+pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots, const void* k_new,
+                         const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,
+                         int32_t kv_heads, int32_t head_dim, pkv_dtype dtype, void* stream) {
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "unknown dtype %d", (int)dtype);
+    if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0");
+    if (kv_heads <= 0 || head_dim <= 0 || head_dim % 8 != 0)
+        return fail(PKV_EINVAL, "kv_heads must be > 0 and head_dim a positive multiple of 8");
+    if (num_slots <= 0) return fail(PKV_EINVAL, "num_slots must be > 0");
+    if (num_tokens == 0) return ok();
+    if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+        return fail(PKV_EINVAL, "null pointer argument");
+    const int64_t row_bytes = (int64_t)kv_heads * head_dim * elem_bytes(dtype);
+    return hip_status(pkv::launch_kv_append(k_cache, v_cache, num_slots, k_new, v_new, num_tokens,
+                                            slot_mapping, row_bytes, (hipStream_t)stream),
+                      "kv_append");
+}
+
+size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                int32_t num_splits) {
+    if (units <= 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || head_dim <= 0) return 0;
+    return make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).ws_bytes;
+}
+
+int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                            int32_t num_splits) {
+    if (kv_heads <= 0) return 1;
+    return make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).splits;
+}
+
+pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* seqused_k,
+                                 int32_t num_seqs, int32_t max_seqlen_k, const void* k_new,
+                                 const void* v_new, int32_t q_heads, int32_t kv_heads,
+                                 int32_t head_dim, float softmax_scale, int32_t causal,
+                                 int32_t window, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+    pkv_status s = check_heads(q_heads, kv_heads, head_dim, dtype);
+    if (s != PKV_OK) return s;
+    if (block_size != PKV_BLOCK_SIZE) return fail(PKV_EINVAL, "block_size %d: must be 16", block_size);
+    if (num_seqs < 0 || num_seqs > kMaxUnits) return fail(PKV_EINVAL, "num_seqs out of range");
+    if (num_blocks <= 0 || max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "num_blocks and max_blocks_per_seq must be > 0");
+    if (max_seqlen_k < 0) return fail(PKV_EINVAL, "max_seqlen_k must be >= 0");
+    if (num_splits < 0) return fail(PKV_EINVAL, "num_splits must be >= 0");
+    if ((k_new == nullptr) != (v_new == nullptr)) return fail(PKV_EINVAL, "give both k_new and v_new, or neither");
+    if (!isfinite(softmax_scale)) return fail(PKV_EINVAL, "softmax_scale must be finite");
+    const int32_t group = q_heads / kv_heads;
+    if (group > kVecMaxGroup) return fail(PKV_EUNSUPPORTED, "q_heads / kv_heads = %d > 8 in decode", group);
+    if (num_seqs == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_table || !seqused_k)
+        return fail(PKV_EINVAL, "null pointer argument");
+    const Plan pl = make_plan(num_seqs, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    if (workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !workspace))
+        return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.ws_bytes);
+
+    const int64_t cap64 = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
+    const int32_t kv_cap = (int32_t)(cap64 < max_seqlen_k ? cap64 : max_seqlen_k);
+    hipStream_t st = (hipStream_t)stream;
+    if (k_new) {
+        const int64_t row_bytes = (int64_t)kv_heads * head_dim * elem_bytes(dtype);
+        s = hip_status(pkv::launch_kv_append_paged_decode((void*)k_cache, (void*)v_cache, num_blocks,
+                                                          k_new, v_new, num_seqs, block_table,
+                                                          max_blocks_per_seq, seqused_k, kv_cap,
+                                                          row_bytes, st),
+                       "kv_append");
+        if (s != PKV_OK) return s;
+    }
+    pkv::AttnParams p{};
+    p.out = out;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.seqused_k = seqused_k;
+    p.block_table = block_table;
+    p.mode = pkv::kPagedDecode;
+    p.total_q = num_seqs;
+    p.num_units = num_seqs;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.max_seqlen_q = 1;
+    p.kv_cap = kv_cap;
+    p.q_heads = q_heads;
+    p.kv_heads = kv_heads;
+    p.group = group;
+    p.causal = causal != 0;
+    p.window = window > 0 ? window : 0;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    return run_attention(p, dtype, head_dim, pl, workspace, st);
+}
+
+pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* seqused_k, int32_t num_seqs,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t block_size, const int32_t* seq_info,
+                           int32_t num_segments, int32_t rows, int32_t cols, int32_t max_seqlen_q,
+                           int32_t max_seqlen_k, int32_t q_heads, int32_t kv_heads,
+                           int32_t head_dim, float softmax_scale, int32_t causal, int32_t window,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes,
+                           pkv_dtype dtype, void* stream) {
+    pkv_status s = check_heads(q_heads, kv_heads, head_dim, dtype);
+    if (s != PKV_OK) return s;
+    const bool paged = block_table != nullptr;
+    const bool column = seq_info != nullptr;
+    if (paged == column) return fail(PKV_EINVAL, "give exactly one of block_table and seq_info");
+    if (total_q < 0) return fail(PKV_EINVAL, "total_q must be >= 0");
+    if (max_seqlen_q < 1) return fail(PKV_EINVAL, "max_seqlen_q must be >= 1");
+    if (num_splits < 0) return fail(PKV_EINVAL, "num_splits must be >= 0");
+    if (!isfinite(softmax_scale)) return fail(PKV_EINVAL, "softmax_scale must be finite");
+    const int32_t w = window > 0 ? window : 0;
+    int32_t units;
+    if (paged) {
+        if (block_size != PKV_BLOCK_SIZE) return fail(PKV_EINVAL, "block_size %d: must be 16", block_size);
+        if (num_seqs < 0 || num_seqs > kMaxUnits) return fail(PKV_EINVAL, "num_seqs out of range");
+        if (num_blocks <= 0 || max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "num_blocks and max_blocks_per_seq must be > 0");
+        if (max_seqlen_k < 0) return fail(PKV_EINVAL, "max_seqlen_k must be >= 0");
+        if (num_seqs > 0 && (!cu_seqlens_q || !seqused_k)) return fail(PKV_EINVAL, "null pointer argument");
+        units = num_seqs;
+    } else {
+        if (rows <= 0 || cols <= 0) return fail(PKV_EINVAL, "rows and cols must be > 0");
+        if (num_segments < 0) return fail(PKV_EINVAL, "num_segments must be >= 0");
+        if ((int64_t)num_segments > 2 * (int64_t)cols)
+            return fail(PKV_EINVAL, "num_segments %d > 2 * cols (%d)", num_segments, 2 * cols);
+        if (w > 0 && (int64_t)rows < (int64_t)w + max_seqlen_q - 1)
+            return fail(PKV_EINVAL, "ring of %d rows cannot hold window %d + max_seqlen_q %d - 1",
+                        rows, w, max_seqlen_q);
+        if (max_seqlen_k <= 0) return fail(PKV_EINVAL, "max_seqlen_k must be > 0 (bound on keys a segment sees)");
+        units = num_segments;
+    }
+    const int32_t group = q_heads / kv_heads;
+    if (max_seqlen_q > 1 || group > kVecMaxGroup)
+        return fail(PKV_EUNSUPPORTED, "multi-row units (max_seqlen_q %d, group %d) need the matrix-core path",
+                    max_seqlen_q, group);
+    if (total_q == 0) return ok();
+    if (!out || !q || !k || !v) return fail(PKV_EINVAL, "null pointer argument");
+    const Plan pl = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    if (workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !workspace))
+        return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.ws_bytes);
+
+    pkv::AttnParams p{};
+    p.out = out;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.total_q = total_q;
+    p.num_units = units;
+    p.max_seqlen_q = max_seqlen_q;
+    p.q_heads = q_heads;
+    p.kv_heads = kv_heads;
+    p.group = group;
+    p.causal = causal != 0;
+    p.window = w;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    if (paged) {
+        p.mode = pkv::kPagedVarlen;
+        p.cu_seqlens_q = cu_seqlens_q;
+        p.seqused_k = seqused_k;
+        p.block_table = block_table;
+        p.max_blocks = max_blocks_per_seq;
+        p.num_blocks = num_blocks;
+        const int64_t cap64 = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
+        p.kv_cap = (int32_t)(cap64 < max_seqlen_k ? cap64 : max_seqlen_k);
+    } else {
+        p.mode = pkv::kColumn;
+        p.seq_info = seq_info;
+        p.rows = rows;
+        p.cols = cols;
+    }
+    return run_attention(p, dtype, head_dim, pl, workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Device helpers for gfx950: raw 16-byte loads, bf16 packing, dot2, DPP
+// cross-lane reductions on wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+struct alignas(16) u32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ uint32_t word(const u32x4& v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// bf16 halves of a 32-bit word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+}
+
+// Two fp32 values rounded to bf16 and packed (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// Round an fp32 value to the nearest bf16 value, kept in fp32.
+__device__ __forceinline__ float round_bf16(float f) {
+    return __builtin_bit_cast(float, f32_to_bf16_bits(f) << 16);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi with bf16 inputs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Gather the low (or high) bf16 of two words into one word: lo from a, hi from b.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- DPP lane permutations (all lanes read a valid source) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- 7-i within 8
+constexpr int kRowMirror = 0x140;     // lane i <- 15-i within 16
+constexpr int kRowRor4 = 0x124;       // lane i <- (i+4)%16 within a row
+constexpr int kRowRor8 = 0x128;       // lane i <- (i+8)%16 within a row
+
+__device__ __forceinline__ float swz_xor16(float x) {
+    // ds_swizzle bitmask mode: and 0x1F, or 0, xor 0x10 (within 32-lane halves)
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32, 64);
+// every lane of a group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (N >= 2) x += dpp<kQuadXor1>(x);
+    if constexpr (N >= 4) x += dpp<kQuadXor2>(x);
+    if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
+    if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+    if constexpr (N >= 32) x += swz_xor16(x);
+    if constexpr (N >= 64) x += xor32(x);
+    return x;
+}
+
+// Over lanes that share (lane % STRIDE): combine the 64/STRIDE lanes
+// l, l+STRIDE, ... (STRIDE = 4, 8, 16, 32, 64); every lane receives the result.
+template <int STRIDE, bool MAX>
+__device__ __forceinline__ float across_groups(float x) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if constexpr (STRIDE <= 8) x = op(x, dpp<kRowRor8>(x));
+    if constexpr (STRIDE <= 4) x = op(x, dpp<kRowRor4>(x));
+    if constexpr (STRIDE <= 16) x = op(x, swz_xor16(x));
+    if constexpr (STRIDE <= 32) x = op(x, xor32(x));
+    return x;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace pkv

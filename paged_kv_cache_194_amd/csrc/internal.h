@@ -1,0 +1,113 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+
+namespace pkv {
+
+// How a unit (a sequence or a segment) finds its query rows and keys.
+enum AddrMode : int32_t {
+    kPagedDecode = 0,   // one query row per sequence, row b; block table
+    kPagedVarlen = 1,   // rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; block table
+    kColumn = 2,        // seq_info (q_start, q_len, col, kv_end); ring column store
+};
+
+// Everything an attention kernel reads, passed by value.
+struct AttnParams {
+    void* out;
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* cu_seqlens_q;
+    const int32_t* seqused_k;
+    const int32_t* block_table;
+    const int32_t* seq_info;
+    float* ws_o;           // split-K partial outputs [units*Hkv*splits][GT][D]
+    float* ws_ml;          // split-K partial (max, sum) [units*Hkv*splits][GT][2]
+    int32_t mode;
+    int32_t total_q;
+    int32_t num_units;
+    int32_t max_blocks;    // block-table row width (paged)
+    int32_t num_blocks;    // pool blocks (paged)
+    int32_t rows;          // ring rows (column)
+    int32_t cols;          // store columns (column)
+    int32_t max_seqlen_q;
+    int32_t kv_cap;        // clamp for seqused_k (paged)
+    int32_t q_heads;
+    int32_t kv_heads;
+    int32_t group;         // q_heads / kv_heads
+    int32_t causal;
+    int32_t window;
+    int32_t num_splits;
+    float scale_log2;      // softmax_scale * log2(e)
+};
+
+// Where one unit's rows and keys are, resolved on the device.
+struct UnitInfo {
+    int32_t q_start;
+    int32_t q_len;
+    int32_t kv_end;        // E after clamping
+    int32_t col;           // column mode only
+    bool keys_ok;          // column inside the store (column mode); true otherwise
+};
+
+__device__ __forceinline__ UnitInfo load_unit(const AttnParams& p, int32_t u) {
+    UnitInfo ui;
+    ui.col = 0;
+    ui.keys_ok = true;
+    if (p.mode == kColumn) {
+        const int32_t* s = p.seq_info + 4 * (int64_t)u;
+        ui.q_start = s[0];
+        ui.q_len = s[1];
+        ui.col = s[2];
+        ui.kv_end = s[3] < 0 ? 0 : s[3];
+        ui.keys_ok = (ui.col >= 0) && (ui.col < p.cols);
+    } else {
+        if (p.mode == kPagedDecode) {
+            ui.q_start = u;
+            ui.q_len = 1;
+        } else {
+            ui.q_start = p.cu_seqlens_q[u];
+            ui.q_len = p.cu_seqlens_q[u + 1] - ui.q_start;
+        }
+        int32_t e = p.seqused_k[u];
+        ui.kv_end = e < 0 ? 0 : (e > p.kv_cap ? p.kv_cap : e);
+    }
+    return ui;
+}
+
+// ---- launchers (each returns hipGetLastError() of its launch) ----
+
+hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
+                            const void* k_new, const void* v_new, int32_t num_tokens,
+                            const int64_t* slot_mapping, int64_t row_bytes, hipStream_t stream);
+
+// Append token b's K/V at position seqused_k[b]-1 of sequence b through its
+// block table (the fused append of a decode step).
+hipError_t launch_kv_append_paged_decode(void* k_cache, void* v_cache, int32_t num_blocks,
+                                         const void* k_new, const void* v_new, int32_t num_seqs,
+                                         const int32_t* block_table, int32_t max_blocks,
+                                         const int32_t* seqused_k, int32_t kv_cap,
+                                         int64_t row_bytes, hipStream_t stream);
+
+// Vector-ALU path for units with one query row (q_len == 1) and group <= 8.
+// Returns hipErrorInvalidValue when no kernel is compiled for (dtype, D, group).
+hipError_t launch_attn_vec(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
+                           hipStream_t stream);
+bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group);
+
+// Log-sum-exp merge of the split-K partials of the vector path.
+hipError_t launch_attn_vec_combine(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
+                                   hipStream_t stream);
+
+// Zero every output row of [0, total_q) that no unit covers.
+hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
+                                 hipStream_t stream);
+
+// Rows of query a vector-path work group holds (group size rounded up).
+int32_t vec_group_rows(int32_t group);
+
+}  // namespace pkv
