@@ -1,0 +1,308 @@
+#!/usr/bin/env python
+"""Decode-attention benchmark on one MI355X.
+
+Default workload: single-sequence bucketed decode at 4K context -- 42 layers,
+32 q / 8 kv heads, head_dim 128, bf16, bucket 4096 with an identity block
+table, 4096 live keys.  One step is one replay of a captured graph holding, for
+every layer, the append of this token's K/V at position 4095 and the attention
+of its query over all 4096 keys (the step rewrites the same slot each replay,
+so replays at a fixed length are idempotent).
+
+Printed on one JSON line:
+  value          KV GB/s: the live K+V bytes a step must read (42 x 2 x 4096 x
+                 8 x 128 x 2 B = 704.6 MB), divided by the measured step time;
+  ms_per_step    graph replay time (HIP events, averaged over --steps);
+  roofline       the per-layer attention call: algorithmic bytes per launch /
+                 its average duration, measured with HIP events around graph
+                 replays of 42 back-to-back calls, against 8 TB/s HBM;
+  cpu_baseline   the fp64 CPU oracle on the same step's bits, timed on the host.
+
+Other workloads (--config c3 / c4 / c5) print the same kind of line for the
+64-sequence batched decode, the column-store step and the long-context passes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode attention KV GB/s (% of HBM peak) + µs/step at 4K ctx, 1×MI355X"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_194_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, launches_per_unit: float = 1.0):
+    """HBM bytes per launch from committed PMC summaries, if they were taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(workload)
+    if not rec or rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def copy_ceiling_gbs(torch, nbytes=4 << 30, reps=5) -> float:
+    """A plain device-to-device copy: read + write bytes over time."""
+    a = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    sec = s.elapsed_time(e) / 1e3 / reps
+    del a, b
+    return 2 * (nbytes // 2) / sec / 1e9
+
+
+def time_graph(torch, graph, reps: int) -> float:
+    """Average seconds per replay, HIP events on the current stream."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / reps
+
+
+def capture(torch, fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+# ---------------------------------------------------------------------------
+# 42-layer single-sequence decode at a fixed context
+# ---------------------------------------------------------------------------
+
+def bench_decode_step(args, torch):
+    import paged_kv_cache_194_amd as pkv
+    import workloads
+    from paged_kv_cache_194_amd.harness import DecodeStepGraph, PagedDecodeCache
+
+    m = workloads.DecodeModel()
+    L = args.ctx
+    dev = torch.device("cuda:0")
+    cache = PagedDecodeCache(m.layers, m.q_heads, m.kv_heads, m.head_dim, L, dev, m.dtype,
+                             num_splits=args.splits)
+    for i in range(m.layers):   # the stored prefix (and stale tail) of every layer
+        cache.k[i].copy_(workloads.randn(cache.k[i].shape, m.dtype, workloads.SEED_BASE + 200 + 2 * i, dev))
+        cache.v[i].copy_(workloads.randn(cache.v[i].shape, m.dtype, workloads.SEED_BASE + 201 + 2 * i, dev))
+    cache.set_length(L)
+    inputs = workloads.c2_step_inputs(1, m, dev)[0].contiguous()       # [layers, Hq+2Hkv, D]
+    out = torch.zeros(m.layers, m.q_heads, m.head_dim, dtype=m.dtype, device=dev)
+    runner = DecodeStepGraph(cache, inputs, out)
+
+    for _ in range(max(1, args.warmup)):
+        runner.step()
+    torch.cuda.synchronize()
+    graph = runner._graphs[(cache.bucket, cache.generation)]
+    t_wall0 = time.perf_counter()
+    sec_step = time_graph(torch, graph, args.steps)
+    wall = time.perf_counter() - t_wall0
+
+    kv_bytes_layer = 2 * L * m.kv_heads * m.head_dim * 2
+    kv_bytes_step = m.layers * kv_bytes_layer
+
+    # Dominant kernel: the per-layer attention call, 42 back-to-back in a graph.
+    ws = cache.workspace
+
+    def attn_only():
+        for i in range(m.layers):
+            x = inputs[i]
+            pkv.paged_decode_attn(out[i].unsqueeze(0), x[:m.q_heads].unsqueeze(0), cache.k[i], cache.v[i],
+                                  cache.block_table, cache.seqused, max_seqlen_k=cache.bucket,
+                                  num_splits=args.splits, workspace=ws)
+    g_attn = capture(torch, attn_only)
+    time_graph(torch, g_attn, 3)
+    sec_call = time_graph(torch, g_attn, max(5, args.steps // 2)) / m.layers
+    achieved = kv_bytes_layer / sec_call / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_bytes_step / sec_step / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_step * 1e3, 5),
+        "us_per_step": round(sec_step * 1e6, 2),
+        "pct_hbm_peak": round(100 * kv_bytes_step / sec_step / 1e9 / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "single-sequence bucketed paged decode, 42 layers, append + attend per layer",
+                   "context": L, "bucket": cache.bucket, "layers": m.layers, "q_heads": m.q_heads,
+                   "kv_heads": m.kv_heads, "head_dim": m.head_dim, "block_size": 16,
+                   "num_splits": pkv.attn_num_splits(1, 1, cache.bucket, m.q_heads, m.kv_heads,
+                                                     m.head_dim, args.splits),
+                   "kv_bytes_per_step": kv_bytes_step},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles("decode_step_4k"),
+                     "kernel": "paged_decode_attn call (one layer, 4096 keys)",
+                     "bytes_per_launch": kv_bytes_layer, "us_per_launch": round(sec_call * 1e6, 3)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if args.copy_ceiling:
+        result["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(args, torch, cache, inputs, L, kv_bytes_step)
+    return result
+
+
+def cpu_baseline_decode(args, torch, cache, inputs, L, kv_bytes_step):
+    """The oracle, as it stands, on the same bits: every layer of one step."""
+    import numpy as np
+
+    import oracle
+
+    m_layers = cache.num_layers
+    hq, hkv, D = cache.q_heads, cache.kv_heads, cache.head_dim
+    layers = list(range(min(m_layers, args.cpu_layers)))
+    host = []
+    for i in layers:
+        host.append((inputs[i, :hq].unsqueeze(0).cpu().view(torch.int16).numpy().view(np.uint16),
+                     cache.k[i].cpu().view(torch.int16).numpy().view(np.uint16),
+                     cache.v[i].cpu().view(torch.int16).numpy().view(np.uint16)))
+    bt = cache.block_table.cpu().numpy()
+    cu = np.array([0, 1])
+    used = np.array([L])
+    t0 = time.perf_counter()
+    for q, k, v in host:
+        oracle.paged_attention(q, k, v, bt, cu, used, dtype="bf16", scale=1.0 / D ** 0.5,
+                               max_seqlen_k=cache.bucket)
+    sec = (time.perf_counter() - t0) / len(layers) * m_layers
+    return {"value": round(kv_bytes_step / sec / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle", "sec_per_step": round(sec, 3),
+            "sample": f"{len(layers)} of {m_layers} layers of one step at {L} keys, scaled to the step"}
+
+
+# ---------------------------------------------------------------------------
+# One-call workloads: batched paged decode, column store, long context
+# ---------------------------------------------------------------------------
+
+def bench_single_call(args, torch):
+    import numpy as np
+
+    import paged_kv_cache_194_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    if args.config == "c3":
+        inp = workloads.c3_batched(device=dev)
+        used = inp.seqused_k.cpu().numpy().astype(np.int64)
+        kv_bytes = int(used.sum()) * inp.kv_heads * inp.head_dim * 2 * 2
+        ws = torch.zeros(max(1, pkv.attn_workspace_bytes(inp.num_seqs, 1, inp.max_seqlen_k, inp.q_heads,
+                                                         inp.kv_heads, inp.head_dim, args.splits)),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(inp.q)
+
+        def call():
+            pkv.paged_decode_attn(out, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seqused_k,
+                                  max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale,
+                                  num_splits=args.splits, workspace=ws)
+        name = "batched paged decode, 64 sequences, lengths U[1,8192], 40000-block pool"
+        extra = {"sum_len": int(used.sum())}
+    elif args.config == "c5d":
+        inp = workloads.c5_long(device=dev, decode=True)
+        used = inp.seqused_k.cpu().numpy().astype(np.int64)
+        kv_bytes = int(used.sum()) * inp.kv_heads * inp.head_dim * 2 * 2
+        splits = args.splits or 16
+        ws = torch.zeros(max(1, pkv.attn_workspace_bytes(inp.num_seqs, 1, inp.max_seqlen_k, inp.q_heads,
+                                                         inp.kv_heads, inp.head_dim, splits)),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(inp.q)
+
+        def call():
+            pkv.paged_decode_attn(out, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seqused_k,
+                                  max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale, causal=True,
+                                  num_splits=splits, workspace=ws)
+        name = "long-context decode, 4 sequences 32K/64K, 64 q / 8 kv heads, D 256, 16 splits"
+        extra = {}
+    else:
+        raise SystemExit(f"unknown --config {args.config}")
+    g = capture(torch, call)
+    time_graph(torch, g, max(1, args.warmup))
+    sec = time_graph(torch, g, args.steps)
+    gbs = kv_bytes / sec / 1e9
+    return {"metric": f"{name}: KV GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+            "us_per_call": round(sec * 1e6, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": {"workload": name, "kv_bytes": kv_bytes, **extra},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c5d"])
+    ap.add_argument("--ctx", type=int, default=4096, help="live keys of the 42-layer decode step")
+    ap.add_argument("--splits", type=int, default=0, help="split-K partitions (0: library choice)")
+    ap.add_argument("--cpu-layers", type=int, default=42, help="layers the CPU oracle times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ceiling", action="store_true", help="also time a 4 GiB device copy")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    import paged_kv_cache_194_amd as pkv
+    pkv.lib()        # fail loudly if the library is missing
+    res = bench_decode_step(args, torch) if args.config == "c2" else bench_single_call(args, torch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -118,7 +118,10 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  *                agree to rounding; a fixed split count is deterministic.
  * workspace    : device scratch of at least pkv_attn_workspace_bytes(num_seqs, 1,
  *                max_seqlen_k, q_heads, kv_heads, head_dim, num_splits) bytes
- *                (may be NULL when that is 0).  Its contents need no initialisation.
+ *                (may be NULL when that is 0).  Zero-fill it once before its
+ *                first use: it starts with split-K arrival counters that every
+ *                call leaves at zero again.  Calls that share a workspace must
+ *                not run concurrently (one stream, or ordered streams).
  */
 pkv_status pkv_paged_decode_attn(void* out, const void* q,
                                  const void* k_cache, const void* v_cache,

@@ -151,7 +151,7 @@ def _workspace(ws: Optional[torch.Tensor], need: int, like: torch.Tensor):
     if need == 0:
         return ws, 0 if ws is None else ws.numel() * ws.element_size()
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=like.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=like.device)   # counters start at 0
     _dev(ws)
     return ws, ws.numel() * ws.element_size()
 

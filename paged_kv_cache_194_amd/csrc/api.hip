@@ -60,11 +60,13 @@ int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_s
     return (int32_t)(s < 1 ? 1 : s);
 }
 
+// Split-K workspace: arrival counters, then partial outputs, then (max, sum) pairs.
 size_t vec_workspace(int32_t units, int32_t kv_heads, int32_t group, int32_t head_dim,
                      int32_t splits) {
     if (splits <= 1 || group > kVecMaxGroup) return 0;
     const size_t gt = (size_t)pkv::vec_group_rows(group);
-    return (size_t)units * kv_heads * splits * gt * ((size_t)head_dim + 2) * sizeof(float);
+    return pkv::ticket_bytes(units, kv_heads) +
+           (size_t)units * kv_heads * splits * gt * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 struct Plan {
@@ -87,12 +89,18 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
     p.num_splits = pl.splits;
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
+    p.ws_ticket = nullptr;
     if (pl.splits > 1) {
         const size_t gt = (size_t)pkv::vec_group_rows(p.group);
         const size_t n = (size_t)p.num_units * p.kv_heads * pl.splits * gt;
-        p.ws_o = (float*)workspace;
+        p.ws_ticket = (int32_t*)workspace;
+        p.ws_o = (float*)((char*)workspace + pkv::ticket_bytes(p.num_units, p.kv_heads));
         p.ws_ml = p.ws_o + n * head_dim;
     }
+    // Split ranges follow the live key range: static ranges cut from the key
+    // bound save one dependent load but leave short sequences on few splits.
+    p.static_split = 0;
+    p.nblk_cap = (p.kv_cap + 15) / 16;
     if (p.num_units == 0 && p.total_q == 0) return ok();
     if (p.mode != pkv::kPagedDecode) {
         pkv_status s = hip_status(pkv::launch_zero_uncovered(p, dtype, head_dim, stream), "zero rows");
@@ -101,10 +109,6 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
     if (p.num_units > 0) {
         pkv_status s = hip_status(pkv::launch_attn_vec(p, dtype, head_dim, stream), "attention");
         if (s != PKV_OK) return s;
-        if (pl.splits > 1) {
-            s = hip_status(pkv::launch_attn_vec_combine(p, dtype, head_dim, stream), "combine");
-            if (s != PKV_OK) return s;
-        }
     }
     return ok();
 }
@@ -186,16 +190,9 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, 
     const int64_t cap64 = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
     const int32_t kv_cap = (int32_t)(cap64 < max_seqlen_k ? cap64 : max_seqlen_k);
     hipStream_t st = (hipStream_t)stream;
-    if (k_new) {
-        const int64_t row_bytes = (int64_t)kv_heads * head_dim * elem_bytes(dtype);
-        s = hip_status(pkv::launch_kv_append_paged_decode((void*)k_cache, (void*)v_cache, num_blocks,
-                                                          k_new, v_new, num_seqs, block_table,
-                                                          max_blocks_per_seq, seqused_k, kv_cap,
-                                                          row_bytes, st),
-                       "kv_append");
-        if (s != PKV_OK) return s;
-    }
     pkv::AttnParams p{};
+    p.k_new = k_new;       // appended inside the attention kernel
+    p.v_new = v_new;
     p.out = out;
     p.q = q;
     p.k = k_cache;

@@ -5,26 +5,36 @@
 // sdpa_varlen's column store, window, zeroed rows and split-K): for the query
 // row of a unit and each q head h of kv head g, softmax(q_h . K^T * scale) V
 // over the unit's visible live keys, read through the block table or ring.
+// With k_new/v_new (paged decode) the same kernel first puts this step's K/V
+// at position E-1, as PagedDecodeCache.attend does before attending.
 //
-// Work decomposition: one work group (4 waves) per (split, kv head, unit).  The
-// unit's visible keys, taken as whole 16-token blocks, are cut into `splits`
-// contiguous block ranges; wave w of a work group takes blocks w, w+4, ... of
-// its range, so the reduction order depends only on logical positions (a
-// permuted block table gives bit-identical results).
+// One kernel per call.  Work decomposition: one work group (4 waves) per
+// (split, kv head, unit).  The unit's keys, as whole 16-token blocks, are cut
+// into `splits` contiguous block ranges -- from the static bound [0, ceil(cap/16))
+// when there is no window (so the block-table gather needs no live length and
+// overlaps the seqused_k load), from the live range otherwise.  Wave w of a work
+// group takes blocks w, w+4, ... of its range: the reduction order depends only
+// on logical positions, so a permuted block table gives bit-identical results.
+// Each wave gathers the block ids of all its blocks with one vector load and
+// keeps the next block's K/V loads in flight while it computes the current one.
 //
 // Per block a wave holds the 16 tokens' K for its kv head in registers laid
-// out KLPT lanes per token (so q . k needs only a KLPT-lane DPP reduction), and
-// their V laid out one 16-byte chunk per lane.  All G query heads of the group
-// are scored against the same registers (GQA sharing).  Scores go through an
+// out KLPT lanes per token (q . k needs only a KLPT-lane DPP reduction) and
+// their V one 16-byte chunk per lane.  All G query heads of the group are
+// scored against the same registers (GQA sharing).  Scores go through an
 // online softmax (running max per head, wave-uniform after a cross-lane max);
-// the probabilities move from the K layout to the V layout through a small
-// per-wave LDS slab.  bf16 inputs use v_dot2_f32_bf16 for both products, with
-// the probabilities rounded to bf16 (the sum l uses the same rounded values, so
-// a constant V comes back exactly).  Accumulation is fp32.
+// probabilities move from the K layout to the V layout through a per-wave LDS
+// slab.  bf16 uses v_dot2_f32_bf16 for both products, with probabilities
+// rounded to bf16 (the running sum uses the same rounded values, so a constant
+// V comes back exactly); fp32 uses fma.  Accumulation is fp32.
+//
+// Split-K: each work group leaves (o, m, l) partials; the last work group of a
+// (unit, kv head) to arrive -- an atomic ticket, reset by that work group --
+// merges them with a log-sum-exp weighting and writes the output.
 //
 // Keys outside the visible range never reach the sums: their scores become
 // -inf by selection and their V chunks are replaced by 0, so NaN or Inf
-// garbage in the storage past seqused_k cannot leak.
+// garbage in storage past seqused_k cannot leak.
 #include "internal.h"
 #include "device_util.h"
 
@@ -54,7 +64,19 @@ struct VecCfg {
     static_assert(KTPW <= 16 && KNI * KTPW == 16, "K layout must tile a block");
     static_assert(VTPW <= 16 && VNI * VTPW == 16, "V layout must tile a block");
     static_assert(!kBF16 || (VNI % 2 == 0), "bf16 PV pairs tokens");
+    // V-layout token groups kept apart in LDS for the final merge (<= 32 KiB).
+    static constexpr int vr_fit(int vr) { return 4 * vr * GT * D * 4 <= 32768 || vr == 1 ? vr : vr_fit(vr / 2); }
+    static constexpr int VR = vr_fit(VTPW);
 };
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+    if constexpr (sizeof(T) == 2) {
+        ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+    } else {
+        ((float*)out)[idx] = v;
+    }
+}
 
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
@@ -63,13 +85,32 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
                   KNI = C::KNI, VLPT = C::VLPT, VTPW = C::VTPW, VNI = C::VNI;
 
     __shared__ float sP[kWaves][16 * GT];
-    __shared__ float sO[kWaves][GT][D];
+    __shared__ float sAcc[kWaves][C::VR][GT][D];
+    __shared__ float sLv[kWaves][C::VR][GT];
     __shared__ float sM[kWaves][GT];
-    __shared__ float sL[kWaves][GT];
+    __shared__ int sLast;
 
     const int32_t split = blockIdx.x;
     const int32_t g = blockIdx.y;
     const int32_t u = blockIdx.z;
+    const int lane = lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int kpart = lane % KLPT, ktok = lane / KLPT;
+    const int vpart = lane % VLPT, vtok = lane / VLPT;
+    const int32_t S = p.num_splits;
+    const bool paged = p.mode != kColumn;
+
+    // Static split: the block range and its block ids need no live length.
+    int32_t sb = 0, se = 0;
+    int32_t ids = -1;
+    if (p.static_split) {
+        const int32_t bps = (p.nblk_cap + S - 1) / S;
+        sb = split * bps;
+        se = min(p.nblk_cap, sb + bps);
+        const int32_t blk = sb + wave + kWaves * lane;
+        if (blk < se) ids = p.block_table[(int64_t)u * p.max_blocks + blk];
+    }
+
     const UnitInfo ui = load_unit(p, u);
     if (ui.q_len != 1) return;                      // other units are not this path's
     const int32_t row = ui.q_start;
@@ -77,27 +118,38 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
 
     const int32_t G = p.group;
     const int32_t Hkv = p.kv_heads;
-    const int32_t S = p.num_splits;
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
     // One query at position E-1: keys [lo, E) with the window's lower bound.
     const int32_t lo = (p.window > 0 && E - p.window > 0) ? E - p.window : 0;
     const int32_t hi = E;
-    const int32_t b_first = lo >> 4;
     const int32_t b_end = (hi + 15) >> 4;
-    const int32_t nblk = b_end > b_first ? b_end - b_first : 0;
-    const int32_t bps = (nblk + S - 1) / S;
-    const int32_t sb = b_first + split * bps;
-    const int32_t se = min(b_end, sb + bps);
-
-    const int lane = lane_id();
-    const int wave = threadIdx.x >> 6;
-    const int kpart = lane % KLPT, ktok = lane / KLPT;
-    const int vpart = lane % VLPT, vtok = lane / VLPT;
+    if (p.static_split) {
+        se = min(se, b_end);
+    } else {
+        const int32_t b_first = lo >> 4;
+        const int32_t nblk = b_end > b_first ? b_end - b_first : 0;
+        const int32_t bps = (nblk + S - 1) / S;
+        sb = b_first + split * bps;
+        se = min(b_end, sb + bps);
+        if (paged) {
+            const int32_t blk = sb + wave + kWaves * lane;
+            if (blk < se) ids = p.block_table[(int64_t)u * p.max_blocks + blk];
+        }
+    }
+    // Blocks of this wave: first + 4 i, i < nb.
+    const int32_t first = sb + wave;
+    const int32_t nb = first < se ? (se - first + kWaves - 1) / kWaves : 0;
 
     const uint8_t* __restrict__ Kb = (const uint8_t*)p.k;
     const uint8_t* __restrict__ Vb = (const uint8_t*)p.v;
     const int64_t tok_stride = (int64_t)Hkv * D * EB;        // bytes between tokens of a block
     const int64_t head_off = (int64_t)g * D * EB;
+
+    // Fused append: token E-1 comes from k_new/v_new and is written to its slot.
+    const bool fuse = p.k_new != nullptr && E > 0;
+    const int32_t pn = E - 1;
+    const uint8_t* kn = fuse ? (const uint8_t*)p.k_new + ((int64_t)u * Hkv + g) * D * EB : nullptr;
+    const uint8_t* vn = fuse ? (const uint8_t*)p.v_new + ((int64_t)u * Hkv + g) * D * EB : nullptr;
 
     // q of the group's heads in the K layout: chunk kpart + KLPT*c of each head.
     u32x4 qr[GT][KCH];
@@ -112,55 +164,84 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             }
     }
 
-    float m[GT], l[GT], acc[GT][VEC];
+    // m: running max per head (wave-uniform); acc and lv: this lane's share of
+    // the output numerator and of the softmax denominator, in the V layout.
+    float m[GT], lv[GT], acc[GT][VEC];
 #pragma unroll
     for (int r = 0; r < GT; ++r) {
         m[r] = -INFINITY;
-        l[r] = 0.f;
+        lv[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[r][e] = 0.f;
     }
 
-    for (int32_t blk = sb + wave; blk < se; blk += kWaves) {
-        const int32_t t0 = blk * 16;
-        // ---- storage of this block ----
-        int64_t pbase = 0;
-        int32_t row0 = 0;
-        if (p.mode == kColumn) {
-            row0 = t0 % p.rows;
-        } else {
-            const int32_t id = p.block_table[(int64_t)u * p.max_blocks + blk];
-            if (id < 0 || id >= p.num_blocks) continue;      // no storage: keys contribute nothing
-            pbase = (int64_t)id * 16 * tok_stride + head_off;
+    // Byte offset of token tt of block `blk` (id: its pool block, paged mode).
+    auto tok_addr = [&](int32_t blk, int32_t id, int tt) -> int64_t {
+        if (!paged) {
+            int32_t r = (blk * 16) % p.rows + tt;
+            if (r >= p.rows) r -= p.rows;
+            if (r >= p.rows) r %= p.rows;       // rings shorter than a block
+            return ((int64_t)r * p.cols + ui.col) * tok_stride + head_off;
         }
-        auto tok_addr = [&](int tt) -> int64_t {
-            if (p.mode == kColumn) {
-                int32_t r = row0 + tt;
-                if (r >= p.rows) r -= p.rows;
-                if (r >= p.rows) r %= p.rows;       // rings shorter than a block
-                return ((int64_t)r * p.cols + ui.col) * tok_stride + head_off;
+        return ((int64_t)id * 16 + tt) * tok_stride + head_off;
+    };
+    auto block_id = [&](int i) -> int32_t {
+        if (!paged) return 0;
+        if ((i & 63) == 0 && i > 0) {           // gather the next 64 ids
+            const int32_t blk = first + kWaves * (i + lane);
+            ids = blk < se ? p.block_table[(int64_t)u * p.max_blocks + blk] : -1;
+        }
+        return __builtin_amdgcn_readlane(ids, i & 63);
+    };
+    auto id_ok = [&](int32_t id) { return !paged || (id >= 0 && id < p.num_blocks); };
+
+    auto load = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
+        const int32_t blk = first + kWaves * i;
+        if (!id_ok(id)) return;
+#pragma unroll
+        for (int j = 0; j < KNI; ++j) {
+            const int tt = j * KTPW + ktok;
+            const int64_t a = tok_addr(blk, id, tt);
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) kr[j][c] = ld16(Kb + a + (kpart + KLPT * c) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < VNI; ++j) vr[j] = ld16(Vb + tok_addr(blk, id, j * VTPW + vtok) + vpart * 16);
+        if (fuse && blk == (pn >> 4)) {         // this step's token: from k_new, and stored
+            uint8_t* Kw = (uint8_t*)p.k;
+            uint8_t* Vw = (uint8_t*)p.v;
+#pragma unroll
+            for (int j = 0; j < KNI; ++j) {
+                if (j * KTPW + ktok == (pn & 15)) {
+                    const int64_t a = tok_addr(blk, id, pn & 15);
+#pragma unroll
+                    for (int c = 0; c < KCH; ++c) {
+                        kr[j][c] = ld16(kn + (kpart + KLPT * c) * 16);
+                        st16(Kw + a + (kpart + KLPT * c) * 16, kr[j][c]);
+                    }
+                }
             }
-            return pbase + (int64_t)tt * tok_stride;
-        };
-
-        u32x4 kr[KNI][KCH];
-        u32x4 vr[VNI];
 #pragma unroll
-        for (int i = 0; i < KNI; ++i) {
-            const int64_t a = tok_addr(i * KTPW + ktok);
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) kr[i][c] = ld16(Kb + a + (kpart + KLPT * c) * 16);
+            for (int j = 0; j < VNI; ++j) {
+                if (j * VTPW + vtok == (pn & 15)) {
+                    vr[j] = ld16(vn + vpart * 16);
+                    st16(Vw + tok_addr(blk, id, pn & 15) + vpart * 16, vr[j]);
+                }
+            }
         }
-#pragma unroll
-        for (int i = 0; i < VNI; ++i) vr[i] = ld16(Vb + tok_addr(i * VTPW + vtok) + vpart * 16);
+    };
 
+    float* P = sP[wave];
+    auto process = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
+        if (!id_ok(id)) return;                 // no storage: these keys contribute nothing
+        const int32_t t0 = (first + kWaves * i) * 16;
         const bool full = (t0 >= lo) && (t0 + 16 <= hi);
 
         // ---- scores for every head of the group (all lanes of a token agree) ----
         float s[KNI][GT];
 #pragma unroll
-        for (int i = 0; i < KNI; ++i) {
-            const int32_t t = t0 + i * KTPW + ktok;
+        for (int j = 0; j < KNI; ++j) {
+            const int32_t t = t0 + j * KTPW + ktok;
             const bool vis = full || (t >= lo && t < hi);
 #pragma unroll
             for (int r = 0; r < GT; ++r) {
@@ -170,15 +251,15 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         if constexpr (C::kBF16) {
-                            d = dot2_bf16(word(qr[r][c], w), word(kr[i][c], w), d);
+                            d = dot2_bf16(word(qr[r][c], w), word(kr[j][c], w), d);
                         } else {
                             d = fmaf(__builtin_bit_cast(float, word(qr[r][c], w)),
-                                     __builtin_bit_cast(float, word(kr[i][c], w)), d);
+                                     __builtin_bit_cast(float, word(kr[j][c], w)), d);
                         }
                     }
                 }
                 d = group_sum<KLPT>(d) * p.scale_log2;
-                s[i][r] = vis ? d : -INFINITY;
+                s[j][r] = vis ? d : -INFINITY;
             }
         }
 
@@ -189,106 +270,151 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
         for (int r = 0; r < GT; ++r) {
             float mb = s[0][r];
 #pragma unroll
-            for (int i = 1; i < KNI; ++i) mb = fmaxf(mb, s[i][r]);
+            for (int j = 1; j < KNI; ++j) mb = fmaxf(mb, s[j][r]);
             mb = across_groups<KLPT, true>(mb);
             const float m_new = fmaxf(m[r], mb);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
             alpha[r] = fast_exp2(m[r] - m_use);
             rescale |= (m_new != m[r]);
             m[r] = m_new;
-            float ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < KNI; ++i) {
-                float pr = fast_exp2(s[i][r] - m_use);
+            for (int j = 0; j < KNI; ++j) {
+                float pr = fast_exp2(s[j][r] - m_use);
                 if constexpr (C::kBF16) pr = round_bf16(pr);
-                s[i][r] = pr;
-                ps += pr;
+                s[j][r] = pr;
             }
-            l[r] = l[r] * alpha[r] + ps;
         }
 
         // ---- probabilities from the K layout to the V layout through LDS ----
-        float* P = sP[wave];
         if (kpart == 0) {
 #pragma unroll
-            for (int i = 0; i < KNI; ++i)
+            for (int j = 0; j < KNI; ++j)
 #pragma unroll
-                for (int r = 0; r < GT; ++r) P[(i * KTPW + ktok) * GT + r] = s[i][r];
+                for (int r = 0; r < GT; ++r) P[(j * KTPW + ktok) * GT + r] = s[j][r];
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        float pv[VNI][GT];
-#pragma unroll
-        for (int i = 0; i < VNI; ++i)
-#pragma unroll
-            for (int r = 0; r < GT; ++r) pv[i][r] = P[(i * VTPW + vtok) * GT + r];
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
         if (rescale) {   // wave-uniform: m is identical in every lane
 #pragma unroll
-            for (int r = 0; r < GT; ++r)
+            for (int r = 0; r < GT; ++r) {
+                lv[r] *= alpha[r];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc[r][e] *= alpha[r];
+            }
         }
-
         if (!full) {
 #pragma unroll
-            for (int i = 0; i < VNI; ++i) {
-                const int32_t t = t0 + i * VTPW + vtok;
-                if (!(t >= lo && t < hi)) vr[i] = u32x4{0u, 0u, 0u, 0u};
+            for (int j = 0; j < VNI; ++j) {
+                const int32_t t = t0 + j * VTPW + vtok;
+                if (!(t >= lo && t < hi)) vr[j] = u32x4{0u, 0u, 0u, 0u};
             }
         }
 
         // ---- PV ----
         if constexpr (C::kBF16) {
 #pragma unroll
-            for (int i = 0; i < VNI; i += 2) {
+            for (int j = 0; j < VNI; j += 2) {
+                float pa[GT], pb[GT];
+#pragma unroll
+                for (int r = 0; r < GT; ++r) {
+                    pa[r] = P[(j * VTPW + vtok) * GT + r];
+                    pb[r] = P[((j + 1) * VTPW + vtok) * GT + r];
+                }
                 uint32_t vp[VEC];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    vp[2 * w] = pair_lo(word(vr[i], w), word(vr[i + 1], w));
-                    vp[2 * w + 1] = pair_hi(word(vr[i], w), word(vr[i + 1], w));
+                    vp[2 * w] = pair_lo(word(vr[j], w), word(vr[j + 1], w));
+                    vp[2 * w + 1] = pair_hi(word(vr[j], w), word(vr[j + 1], w));
                 }
 #pragma unroll
                 for (int r = 0; r < GT; ++r) {
-                    const uint32_t pp = pair_hi(__builtin_bit_cast(uint32_t, pv[i][r]),
-                                                __builtin_bit_cast(uint32_t, pv[i + 1][r]));
+                    lv[r] += pa[r] + pb[r];
+                    const uint32_t pp = pair_hi(__builtin_bit_cast(uint32_t, pa[r]),
+                                                __builtin_bit_cast(uint32_t, pb[r]));
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) acc[r][e] = dot2_bf16(pp, vp[e], acc[r][e]);
                 }
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < VNI; ++i)
+            for (int j = 0; j < VNI; ++j) {
 #pragma unroll
-                for (int r = 0; r < GT; ++r)
+                for (int r = 0; r < GT; ++r) {
+                    const float pr = P[(j * VTPW + vtok) * GT + r];
+                    lv[r] += pr;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
-                        acc[r][e] = fmaf(pv[i][r], __builtin_bit_cast(float, word(vr[i], e)), acc[r][e]);
+                        acc[r][e] = fmaf(pr, __builtin_bit_cast(float, word(vr[j], e)), acc[r][e]);
+                }
+            }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+
+    // ---- block loop, next block's loads in flight during the current compute ----
+    {
+        u32x4 ka[KNI][KCH], kb[KNI][KCH], va[VNI], vb[VNI];
+        int32_t ida = 0, idb = 0;
+        if (nb > 0) {
+            ida = block_id(0);
+            load(0, ida, ka, va);
+        }
+        for (int i = 0; i < nb; i += 2) {
+            if (i + 1 < nb) {
+                idb = block_id(i + 1);
+                load(i + 1, idb, kb, vb);
+            }
+            process(i, ida, ka, va);
+            if (i + 1 >= nb) break;
+            if (i + 2 < nb) {
+                ida = block_id(i + 2);
+                load(i + 2, ida, ka, va);
+            }
+            process(i + 1, idb, kb, vb);
         }
     }
 
-    // ---- merge lanes, then waves ----
+    // ---- merge lanes, then waves, through LDS ----
+    // acc and lv: fold the V-layout token groups down to VR groups, park them
+    // in LDS; m is wave-uniform.
+    constexpr int VR = C::VR;
+    auto fold = [&](float x) -> float {
+        if constexpr (VR * VLPT < 64) {
+#pragma unroll
+            for (int st = VR * VLPT; st < 64; st *= 2) {
+                if (st == 1) x += xor_lanes<1>(x);
+                else if (st == 2) x += xor_lanes<2>(x);
+                else if (st == 4) x += xor_lanes<4>(x);
+                else if (st == 8) x += xor_lanes<8>(x);
+                else if (st == 16) x += xor_lanes<16>(x);
+                else x += xor_lanes<32>(x);
+            }
+        }
+        return x;
+    };
 #pragma unroll
     for (int r = 0; r < GT; ++r) {
+        lv[r] = fold(lv[r]);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[r][e] = across_groups<VLPT, false>(acc[r][e]);
-        l[r] = across_groups<KLPT, false>(l[r]);
+        for (int e = 0; e < VEC; ++e) acc[r][e] = fold(acc[r][e]);
     }
-    if (vtok == 0) {
+    if (vtok < VR) {
 #pragma unroll
         for (int r = 0; r < GT; ++r)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) sO[wave][r][vpart * VEC + e] = acc[r][e];
+            for (int e = 0; e < VEC; ++e) sAcc[wave][vtok][r][vpart * VEC + e] = acc[r][e];
+        if (vpart == 0) {
+#pragma unroll
+            for (int r = 0; r < GT; ++r) sLv[wave][vtok][r] = lv[r];
+        }
     }
     if (lane == 0) {
 #pragma unroll
-        for (int r = 0; r < GT; ++r) {
-            sM[wave][r] = m[r];
-            sL[wave][r] = l[r];
-        }
+        for (int r = 0; r < GT; ++r) sM[wave][r] = m[r];
     }
     __syncthreads();
 
+    const int64_t wi = ((int64_t)u * Hkv + g) * S + split;
     for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
         const int r = idx / D, d = idx - (idx / D) * D;
         if (r >= G) continue;
@@ -300,62 +426,91 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float sc = fast_exp2(sM[w][r] - M);
-                o = fmaf(sc, sO[w][r][d], o);
-                lsum = fmaf(sc, sL[w][r], lsum);
+                float ow = 0.f, lw = 0.f;
+#pragma unroll
+                for (int t = 0; t < VR; ++t) {
+                    ow += sAcc[w][t][r][d];
+                    lw += sLv[w][t][r];
+                }
+                o = fmaf(sc, ow, o);
+                lsum = fmaf(sc, lw, lsum);
             }
         }
         if (S == 1) {
-            const float res = lsum > 0.f ? o / lsum : 0.f;
-            const int64_t oi = ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d;
-            if constexpr (C::kBF16) {
-                ((uint16_t*)p.out)[oi] = (uint16_t)f32_to_bf16_bits(res);
-            } else {
-                ((float*)p.out)[oi] = res;
-            }
+            store_out<T>(p.out, ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d,
+                         lsum > 0.f ? o / lsum : 0.f);
         } else {
-            const int64_t wi = ((int64_t)u * Hkv + g) * S + split;
-            p.ws_o[(wi * GT + r) * D + d] = o;
+            st_agent(&p.ws_o[(wi * GT + r) * D + d], o);
             if (d == 0) {
-                p.ws_ml[(wi * GT + r) * 2 + 0] = M;
-                p.ws_ml[(wi * GT + r) * 2 + 1] = lsum;
+                st_agent(&p.ws_ml[(wi * GT + r) * 2 + 0], M);
+                st_agent(&p.ws_ml[(wi * GT + r) * 2 + 1], lsum);
             }
         }
     }
-}
+    if (S == 1) return;
 
-// Merge of the split partials of one (unit, kv head).
-template <typename T, int D, int GT>
-__global__ __launch_bounds__(256) void attn_vec_combine_kernel(AttnParams p) {
-    const int32_t g = blockIdx.x;
-    const int32_t u = blockIdx.y;
-    const UnitInfo ui = load_unit(p, u);
-    if (ui.q_len != 1) return;
-    const int32_t row = ui.q_start;
-    if (row < 0 || row >= p.total_q) return;
-    const int32_t G = p.group, S = p.num_splits;
-    const int64_t w0 = ((int64_t)u * p.kv_heads + g) * S;
-    for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
-        const int r = idx / D, d = idx - (idx / D) * D;
+    // ---- split-K: the last work group of this (unit, kv head) merges ----
+    // Partials went out with device-coherent stores; once every wave's stores
+    // have completed, one thread takes a ticket.  The work group drawing the
+    // last ticket drops its stale cache lines (an agent-scope acquire: no
+    // writeback) and reads all partials with 16-byte loads.
+    wait_vm_all();
+    __syncthreads();
+    int32_t* ticket = p.ws_ticket + ((int64_t)u * Hkv + g);
+    if (threadIdx.x == 0)
+        sLast = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1);
+    __syncthreads();
+    if (!sLast) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (threadIdx.x == 0)                       // ready for the next call
+        __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Each thread merges 4 consecutive outputs of one head over all splits, 16
+    // splits' (m, l, o) in flight at a time (indices past S are clamped and
+    // weighted 0), with a running max across chunks.
+    const int64_t w0 = ((int64_t)u * Hkv + g) * S;
+    constexpr int CH = 32;
+    for (int idx = threadIdx.x; idx < GT * (D / 4); idx += kThreads) {
+        const int r = idx / (D / 4), d4 = (idx - r * (D / 4)) * 4;
         if (r >= G) continue;
-        float M = -INFINITY;
-        for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[((w0 + s) * GT + r) * 2]);
-        float o = 0.f, lsum = 0.f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < S; ++s) {
-                const float ms = p.ws_ml[((w0 + s) * GT + r) * 2];
-                if (ms == -INFINITY) continue;           // empty split: its o/l are not read
-                const float sc = fast_exp2(ms - M);
-                o = fmaf(sc, p.ws_o[((w0 + s) * GT + r) * D + d], o);
-                lsum = fmaf(sc, p.ws_ml[((w0 + s) * GT + r) * 2 + 1], lsum);
+        const float* osrc = p.ws_o + (w0 * GT + r) * D + d4;
+        const float* msrc = p.ws_ml + (w0 * GT + r) * 2;
+        const int64_t ostride = (int64_t)GT * D, mstride = (int64_t)GT * 2;
+        float M = -INFINITY, tot = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < S; s0 += CH) {
+            float2 ml[CH];
+            float4 x[CH];
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const int sk = min(s0 + k, S - 1);
+                ml[k] = *reinterpret_cast<const float2*>(msrc + sk * mstride);
+                x[k] = *reinterpret_cast<const float4*>(osrc + sk * ostride);
             }
+            float Mc = M;
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+                if (s0 + k < S) Mc = fmaxf(Mc, ml[k].x);
+            if (Mc == -INFINITY) continue;      // nothing visible yet
+            const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mc);
+            tot *= a;
+            o.x *= a; o.y *= a; o.z *= a; o.w *= a;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const float w = (s0 + k < S && ml[k].x != -INFINITY) ? fast_exp2(ml[k].x - Mc) : 0.f;
+                tot = fmaf(w, ml[k].y, tot);
+                o.x = fmaf(w, x[k].x, o.x);
+                o.y = fmaf(w, x[k].y, o.y);
+                o.z = fmaf(w, x[k].z, o.z);
+                o.w = fmaf(w, x[k].w, o.w);
+            }
+            M = Mc;
         }
-        const float res = lsum > 0.f ? o / lsum : 0.f;
-        const int64_t oi = ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d;
-        if constexpr (sizeof(T) == 2) {
-            ((uint16_t*)p.out)[oi] = (uint16_t)f32_to_bf16_bits(res);
-        } else {
-            ((float*)p.out)[oi] = res;
-        }
+        const float inv = tot > 0.f ? 1.f / tot : 0.f;
+        const int64_t oi = ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d4;
+        store_out<T>(p.out, oi + 0, o.x * inv);
+        store_out<T>(p.out, oi + 1, o.y * inv);
+        store_out<T>(p.out, oi + 2, o.z * inv);
+        store_out<T>(p.out, oi + 3, o.w * inv);
     }
 }
 
@@ -387,6 +542,11 @@ int32_t vec_group_rows(int32_t group) {
     return group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
 }
 
+size_t ticket_bytes(int32_t units, int32_t kv_heads) {
+    const size_t n = (size_t)units * kv_heads * sizeof(int32_t);
+    return (n + 255) / 256 * 256;
+}
+
 bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group) {
     return (dtype == PKV_F32 || dtype == PKV_BF16) &&
            (head_dim == 64 || head_dim == 128 || head_dim == 256) && group >= 1 && group <= 8;
@@ -396,13 +556,6 @@ template <typename T, int D, int GT>
 static hipError_t launch_vec_t(const AttnParams& p, hipStream_t stream) {
     dim3 grid(p.num_splits, p.kv_heads, p.num_units);
     attn_vec_kernel<T, D, GT><<<grid, dim3(kThreads), 0, stream>>>(p);
-    return hipGetLastError();
-}
-
-template <typename T, int D, int GT>
-static hipError_t launch_combine_t(const AttnParams& p, hipStream_t stream) {
-    dim3 grid(p.kv_heads, p.num_units);
-    attn_vec_combine_kernel<T, D, GT><<<grid, dim3(256), 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -449,12 +602,6 @@ static hipError_t launch_combine_t(const AttnParams& p, hipStream_t stream) {
 hipError_t launch_attn_vec(const AttnParams& p, pkv_dtype dtype, int32_t head_dim, hipStream_t stream) {
     if (!attn_vec_supported(dtype, head_dim, p.group)) return hipErrorInvalidValue;
     PKV_DISPATCH(launch_vec_t, dtype, head_dim, p.group, p, stream);
-}
-
-hipError_t launch_attn_vec_combine(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
-                                   hipStream_t stream) {
-    if (!attn_vec_supported(dtype, head_dim, p.group)) return hipErrorInvalidValue;
-    PKV_DISPATCH(launch_combine_t, dtype, head_dim, p.group, p, stream);
 }
 
 hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,

@@ -80,6 +80,18 @@ __device__ __forceinline__ float swz_xor16(float x) {
 }
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// x from lane (lane ^ ST), ST = 1 .. 32.
+template <int ST>
+__device__ __forceinline__ float xor_lanes(float x) {
+    if constexpr (ST == 32) {
+        return xor32(x);
+    } else {
+        // ds_swizzle bitmask mode (within 32-lane halves): and 0x1F, or 0, xor ST
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
+                                                                     0x1F | (ST << 10)));
+    }
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32, 64);
 // every lane of a group receives the group's sum.
 template <int N>
@@ -106,5 +118,18 @@ __device__ __forceinline__ float across_groups(float x) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Device-coherent (agent scope) word access.  On gfx950 these are plain loads
+// and stores with the sc1 scope bit: they bypass the per-XCD L2's
+// non-coherent lines without the whole-cache writeback/invalidate that a
+// device-scope fence costs.  Used to hand split-K partials between work groups.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory access this wave issued has completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace pkv

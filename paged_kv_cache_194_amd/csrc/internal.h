@@ -25,8 +25,11 @@ struct AttnParams {
     const int32_t* seqused_k;
     const int32_t* block_table;
     const int32_t* seq_info;
+    const void* k_new;     // fused append (paged decode): [units, Hkv, D] or null
+    const void* v_new;
     float* ws_o;           // split-K partial outputs [units*Hkv*splits][GT][D]
     float* ws_ml;          // split-K partial (max, sum) [units*Hkv*splits][GT][2]
+    int32_t* ws_ticket;    // per (unit, kv head) arrival counters, zero between calls
     int32_t mode;
     int32_t total_q;
     int32_t num_units;
@@ -42,6 +45,8 @@ struct AttnParams {
     int32_t causal;
     int32_t window;
     int32_t num_splits;
+    int32_t static_split;  // 1: split ranges cut from [0, nblk_cap) (no window, paged)
+    int32_t nblk_cap;      // ceil(kv_cap / 16)
     float scale_log2;      // softmax_scale * log2(e)
 };
 
@@ -85,23 +90,11 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
                             const void* k_new, const void* v_new, int32_t num_tokens,
                             const int64_t* slot_mapping, int64_t row_bytes, hipStream_t stream);
 
-// Append token b's K/V at position seqused_k[b]-1 of sequence b through its
-// block table (the fused append of a decode step).
-hipError_t launch_kv_append_paged_decode(void* k_cache, void* v_cache, int32_t num_blocks,
-                                         const void* k_new, const void* v_new, int32_t num_seqs,
-                                         const int32_t* block_table, int32_t max_blocks,
-                                         const int32_t* seqused_k, int32_t kv_cap,
-                                         int64_t row_bytes, hipStream_t stream);
-
 // Vector-ALU path for units with one query row (q_len == 1) and group <= 8.
 // Returns hipErrorInvalidValue when no kernel is compiled for (dtype, D, group).
 hipError_t launch_attn_vec(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
                            hipStream_t stream);
 bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group);
-
-// Log-sum-exp merge of the split-K partials of the vector path.
-hipError_t launch_attn_vec_combine(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
-                                   hipStream_t stream);
 
 // Zero every output row of [0, total_q) that no unit covers.
 hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
@@ -109,5 +102,8 @@ hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t h
 
 // Rows of query a vector-path work group holds (group size rounded up).
 int32_t vec_group_rows(int32_t group);
+
+// Bytes of the arrival counters at the start of a split-K workspace.
+size_t ticket_bytes(int32_t units, int32_t kv_heads);
 
 }  // namespace pkv

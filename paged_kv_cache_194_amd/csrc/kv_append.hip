@@ -28,30 +28,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     st16(v_cache + dst, ld16(v_new + src));
 }
 
-// Decode-step append: sequence b's new token sits at position seqused_k[b]-1;
-// its slot is found through the sequence's block table.
-__global__ __launch_bounds__(256) void kv_append_paged_decode_kernel(
-    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, int32_t num_blocks,
-    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
-    int32_t chunks_per_row, const int32_t* __restrict__ block_table, int32_t max_blocks,
-    const int32_t* __restrict__ seqused_k, int32_t kv_cap) {
-    const int32_t b = blockIdx.y;
-    const int32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= chunks_per_row) return;
-    int32_t e = seqused_k[b];
-    e = e < 0 ? 0 : (e > kv_cap ? kv_cap : e);
-    if (e == 0) return;
-    const int32_t pos = e - 1;
-    const int32_t blk = block_table[(int64_t)b * max_blocks + (pos >> 4)];
-    if (blk < 0 || blk >= num_blocks) return;
-    const int64_t slot = (int64_t)blk * 16 + (pos & 15);
-    const int64_t row_bytes = (int64_t)chunks_per_row * 16;
-    const int64_t src = (int64_t)b * row_bytes + (int64_t)c * 16;
-    const int64_t dst = slot * row_bytes + (int64_t)c * 16;
-    st16(k_cache + dst, ld16(k_new + src));
-    st16(v_cache + dst, ld16(v_new + src));
-}
-
 hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
                             const void* k_new, const void* v_new, int32_t num_tokens,
                             const int64_t* slot_mapping, int64_t row_bytes, hipStream_t stream) {
@@ -61,19 +37,6 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
     kv_append_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
         (uint8_t*)k_cache, (uint8_t*)v_cache, num_slots, (const uint8_t*)k_new,
         (const uint8_t*)v_new, total, cpr, slot_mapping);
-    return hipGetLastError();
-}
-
-hipError_t launch_kv_append_paged_decode(void* k_cache, void* v_cache, int32_t num_blocks,
-                                         const void* k_new, const void* v_new, int32_t num_seqs,
-                                         const int32_t* block_table, int32_t max_blocks,
-                                         const int32_t* seqused_k, int32_t kv_cap,
-                                         int64_t row_bytes, hipStream_t stream) {
-    const int32_t cpr = (int32_t)(row_bytes / 16);
-    dim3 grid((cpr + 255) / 256, num_seqs);
-    kv_append_paged_decode_kernel<<<grid, dim3(256), 0, stream>>>(
-        (uint8_t*)k_cache, (uint8_t*)v_cache, num_blocks, (const uint8_t*)k_new,
-        (const uint8_t*)v_new, cpr, block_table, max_blocks, seqused_k, kv_cap);
     return hipGetLastError();
 }
 

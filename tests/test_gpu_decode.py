@@ -361,7 +361,7 @@ def test_graph_replay_matches_eager_across_lengths():
     kn = torch.zeros(1, H, D, dtype=torch.bfloat16, device=dev)
     vn = torch.zeros(1, H, D, dtype=torch.bfloat16, device=dev)
     out = torch.zeros(1, hq, D, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(pkv.attn_workspace_bytes(1, 1, bucket, hq, H, D), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(pkv.attn_workspace_bytes(1, 1, bucket, hq, H, D), dtype=torch.uint8, device=dev)
     steps = workloads.randn((40, hq + 2 * H, D), torch.bfloat16, 73, dev)
 
     def step():
@@ -396,3 +396,23 @@ def test_graph_replay_matches_eager_across_lengths():
         ref = oracle.paged_attention(raw(q), raw(k), raw(v), bt.cpu().numpy(), np.array([0, 1]),
                                      np.array([L]), dtype="bf16", scale=1 / D ** 0.5, max_seqlen_k=bucket)
         check_close(got, ref, "bf16", f"graph length {L}")
+
+
+def test_split_tickets_reset_and_workspace_reuse():
+    """Split-K arrival counters come back to zero after every call, so one
+    zero-filled workspace serves many calls and split counts in a row."""
+    inp = workloads.paged_inputs(seed=81, lengths=[3000, 17, 900, 1], q_lens=[1] * 4, q_heads=32, kv_heads=8,
+                                 head_dim=128, dtype=torch.bfloat16, num_blocks=300, max_blocks=192, device=DEV)
+    ref = oracle_paged(inp)
+    ws = torch.zeros(pkv.attn_workspace_bytes(4, 1, inp.max_seqlen_k, 32, 8, 128, 64), dtype=torch.uint8,
+                     device=DEV)
+    first = None
+    for s in (64, 2, 7, 64, 33):
+        out = run_decode(inp, num_splits=s, workspace=ws)
+        check_close(out, ref, "bf16", f"splits={s}")
+        assert int(ws[:4 * 8 * 4].view(torch.int32).abs().sum()) == 0
+        if s == 64:
+            if first is None:
+                first = out.clone()
+            else:
+                assert torch.equal(bits(out), bits(first))
