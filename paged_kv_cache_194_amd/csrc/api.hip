@@ -49,65 +49,101 @@ pkv_status check_heads(int32_t q_heads, int32_t kv_heads, int32_t head_dim, pkv_
     return PKV_OK;
 }
 
-int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_splits) {
-    if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
-    const int64_t base = (int64_t)(units > 0 ? units : 1) * kv_heads;
-    const int64_t blocks = ((int64_t)(keys > 0 ? keys : 1) + 15) / 16;
-    int64_t s = (2048 + base - 1) / base;        // about 2048 work groups
-    const int64_t cap = blocks / 4 > 0 ? blocks / 4 : 1;   // >= 4 blocks (1 per wave) each
+int32_t clamp_splits(int64_t s, int64_t cap) {
     if (s > cap) s = cap;
     if (s > kMaxSplits) s = kMaxSplits;
     return (int32_t)(s < 1 ? 1 : s);
 }
 
-// Split-K workspace: arrival counters, then partial outputs, then (max, sum) pairs.
-size_t vec_workspace(int32_t units, int32_t kv_heads, int32_t group, int32_t head_dim,
-                     int32_t splits) {
-    if (splits <= 1 || group > kVecMaxGroup) return 0;
-    const size_t gt = (size_t)pkv::vec_group_rows(group);
-    return pkv::ticket_bytes(units, kv_heads) +
-           (size_t)units * kv_heads * splits * gt * ((size_t)head_dim + 2) * sizeof(float);
+// Vector path: about 2048 work groups, at least 4 blocks (one per wave) each.
+int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_splits) {
+    if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
+    const int64_t base = (int64_t)(units > 0 ? units : 1) * kv_heads;
+    const int64_t blocks = ((int64_t)(keys > 0 ? keys : 1) + 15) / 16;
+    return clamp_splits((2048 + base - 1) / base, blocks / 4 > 0 ? blocks / 4 : 1);
 }
 
+// Plan of one attention call: which paths run, their split counts and the
+// workspace layout (vector tickets | vector partials | mfma tickets | mfma partials).
 struct Plan {
-    int32_t splits;
+    bool vec, mfma;
+    int32_t splits;          // vector path
+    int32_t gt;              // vector path rows per work group
+    int32_t tiles, msplits;  // matrix-core path
+    int32_t bm;
+    size_t vec_ticket, vec_bytes, mfma_ticket, mfma_bytes;
     size_t ws_bytes;
 };
 
 Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_heads, int32_t kv_heads,
                int32_t head_dim, int32_t num_splits) {
-    Plan pl;
+    Plan pl{};
+    const int32_t group = q_heads / kv_heads;
+    const int32_t U = units > 0 ? units : 1;
+    pl.vec = group <= kVecMaxGroup;
+    pl.mfma = max_seqlen_q > 1 || group > kVecMaxGroup;
     pl.splits = pick_splits(units, kv_heads, keys, num_splits);
-    pl.ws_bytes = vec_workspace(units, kv_heads, q_heads / kv_heads, head_dim, pl.splits);
-    (void)max_seqlen_q;
+    pl.gt = pkv::vec_group_rows(group);
+    if (pl.vec && pl.splits > 1) {
+        pl.vec_ticket = pkv::ticket_bytes(U, kv_heads);
+        pl.vec_bytes = (size_t)U * kv_heads * pl.splits * pl.gt * ((size_t)head_dim + 2) * sizeof(float);
+    }
+    if (pl.mfma) {
+        pl.bm = pkv::mfma_rows_per_group(head_dim);
+        const int64_t rows = (int64_t)max_seqlen_q * group;
+        pl.tiles = (int32_t)((rows + pl.bm - 1) / pl.bm);
+        const int64_t base = (int64_t)U * kv_heads * pl.tiles;
+        const int64_t chunks = ((int64_t)(keys > 0 ? keys : 1) + pkv::mfma_chunk_keys(head_dim) - 1) /
+                               pkv::mfma_chunk_keys(head_dim);
+        pl.msplits = num_splits > 0 ? clamp_splits(num_splits, chunks)
+                                    : clamp_splits((512 + base - 1) / base, chunks / 2 > 0 ? chunks / 2 : 1);
+        if (pl.msplits > 1) {
+            pl.mfma_ticket = pkv::ticket_bytes(U * pl.tiles, kv_heads);
+            pl.mfma_bytes = (size_t)base * pl.msplits * pl.bm * ((size_t)head_dim + 2) * sizeof(float);
+        }
+    } else {
+        pl.tiles = 0;
+        pl.msplits = 1;
+    }
+    pl.ws_bytes = pl.vec_ticket + pl.vec_bytes + pl.mfma_ticket + pl.mfma_bytes;
     return pl;
 }
 
 // Enqueue the attention kernels for a fully checked parameter block.
 pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, const Plan& pl,
                          void* workspace, hipStream_t stream) {
+    char* ws = (char*)workspace;
     p.num_splits = pl.splits;
-    p.ws_o = nullptr;
-    p.ws_ml = nullptr;
     p.ws_ticket = nullptr;
-    if (pl.splits > 1) {
-        const size_t gt = (size_t)pkv::vec_group_rows(p.group);
-        const size_t n = (size_t)p.num_units * p.kv_heads * pl.splits * gt;
-        p.ws_ticket = (int32_t*)workspace;
-        p.ws_o = (float*)((char*)workspace + pkv::ticket_bytes(p.num_units, p.kv_heads));
+    p.ws_o = p.ws_ml = nullptr;
+    if (pl.vec_bytes) {
+        const size_t n = (size_t)p.num_units * p.kv_heads * pl.splits * pl.gt;
+        p.ws_ticket = (int32_t*)ws;
+        p.ws_o = (float*)(ws + pl.vec_ticket);
         p.ws_ml = p.ws_o + n * head_dim;
     }
-    // Split ranges follow the live key range: static ranges cut from the key
-    // bound save one dependent load but leave short sequences on few splits.
-    p.static_split = 0;
-    p.nblk_cap = (p.kv_cap + 15) / 16;
+    p.mfma_tiles = pl.tiles;
+    p.mfma_splits = pl.msplits;
+    p.mws_ticket = nullptr;
+    p.mws_o = p.mws_ml = nullptr;
+    if (pl.mfma_bytes) {
+        char* base = ws + pl.vec_ticket + pl.vec_bytes;
+        const size_t n = (size_t)p.num_units * p.kv_heads * pl.tiles * pl.msplits * pl.bm;
+        p.mws_ticket = (int32_t*)base;
+        p.mws_o = (float*)(base + pl.mfma_ticket);
+        p.mws_ml = p.mws_o + n * head_dim;
+    }
     if (p.num_units == 0 && p.total_q == 0) return ok();
     if (p.mode != pkv::kPagedDecode) {
         pkv_status s = hip_status(pkv::launch_zero_uncovered(p, dtype, head_dim, stream), "zero rows");
         if (s != PKV_OK) return s;
     }
-    if (p.num_units > 0) {
+    if (p.num_units > 0 && pl.vec) {
         pkv_status s = hip_status(pkv::launch_attn_vec(p, dtype, head_dim, stream), "attention");
+        if (s != PKV_OK) return s;
+    }
+    if (p.num_units > 0 && pl.mfma) {
+        pkv_status s = hip_status(pkv::launch_attn_mfma(p, dtype, head_dim, stream), "attention (mfma)");
         if (s != PKV_OK) return s;
     }
     return ok();
@@ -179,7 +215,10 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, 
     if ((k_new == nullptr) != (v_new == nullptr)) return fail(PKV_EINVAL, "give both k_new and v_new, or neither");
     if (!isfinite(softmax_scale)) return fail(PKV_EINVAL, "softmax_scale must be finite");
     const int32_t group = q_heads / kv_heads;
-    if (group > kVecMaxGroup) return fail(PKV_EUNSUPPORTED, "q_heads / kv_heads = %d > 8 in decode", group);
+    if (group > kVecMaxGroup && !pkv::attn_mfma_supported(dtype, head_dim))
+        return fail(PKV_EUNSUPPORTED, "q_heads / kv_heads = %d > 8 needs bf16 (matrix-core path)", group);
+    if (group > kVecMaxGroup && k_new)
+        return fail(PKV_EUNSUPPORTED, "fused append with q_heads / kv_heads > 8: call pkv_kv_append first");
     if (num_seqs == 0) return ok();
     if (!out || !q || !k_cache || !v_cache || !block_table || !seqused_k)
         return fail(PKV_EINVAL, "null pointer argument");
@@ -254,8 +293,8 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q, const void
         units = num_segments;
     }
     const int32_t group = q_heads / kv_heads;
-    if (max_seqlen_q > 1 || group > kVecMaxGroup)
-        return fail(PKV_EUNSUPPORTED, "multi-row units (max_seqlen_q %d, group %d) need the matrix-core path",
+    if ((max_seqlen_q > 1 || group > kVecMaxGroup) && !pkv::attn_mfma_supported(dtype, head_dim))
+        return fail(PKV_EUNSUPPORTED, "multi-row units (max_seqlen_q %d, group %d) run on the bf16 matrix-core path",
                     max_seqlen_q, group);
     if (total_q == 0) return ok();
     if (!out || !q || !k || !v) return fail(PKV_EINVAL, "null pointer argument");

@@ -78,7 +78,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     }
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     using C = VecCfg<T, D, GT>;
     constexpr int EB = C::EB, VEC = C::VEC, KLPT = C::KLPT, KCH = C::KCH, KTPW = C::KTPW,
@@ -98,18 +98,6 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     const int kpart = lane % KLPT, ktok = lane / KLPT;
     const int vpart = lane % VLPT, vtok = lane / VLPT;
     const int32_t S = p.num_splits;
-    const bool paged = p.mode != kColumn;
-
-    // Static split: the block range and its block ids need no live length.
-    int32_t sb = 0, se = 0;
-    int32_t ids = -1;
-    if (p.static_split) {
-        const int32_t bps = (p.nblk_cap + S - 1) / S;
-        sb = split * bps;
-        se = min(p.nblk_cap, sb + bps);
-        const int32_t blk = sb + wave + kWaves * lane;
-        if (blk < se) ids = p.block_table[(int64_t)u * p.max_blocks + blk];
-    }
 
     const UnitInfo ui = load_unit(p, u);
     if (ui.q_len != 1) return;                      // other units are not this path's
@@ -123,18 +111,15 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     const int32_t lo = (p.window > 0 && E - p.window > 0) ? E - p.window : 0;
     const int32_t hi = E;
     const int32_t b_end = (hi + 15) >> 4;
-    if (p.static_split) {
-        se = min(se, b_end);
-    } else {
-        const int32_t b_first = lo >> 4;
-        const int32_t nblk = b_end > b_first ? b_end - b_first : 0;
-        const int32_t bps = (nblk + S - 1) / S;
-        sb = b_first + split * bps;
-        se = min(b_end, sb + bps);
-        if (paged) {
-            const int32_t blk = sb + wave + kWaves * lane;
-            if (blk < se) ids = p.block_table[(int64_t)u * p.max_blocks + blk];
-        }
+    const int32_t b_first = lo >> 4;
+    const int32_t nblk = b_end > b_first ? b_end - b_first : 0;
+    const int32_t bps = (nblk + S - 1) / S;
+    const int32_t sb = b_first + split * bps;
+    const int32_t se = min(b_end, sb + bps);
+    int32_t ids = -1;               // lane i: pool block of this wave's i-th block
+    if constexpr (PAGED) {
+        const int32_t blk = sb + wave + kWaves * lane;
+        if (blk < se) ids = p.block_table[(int64_t)u * p.max_blocks + blk];
     }
     // Blocks of this wave: first + 4 i, i < nb.
     const int32_t first = sb + wave;
@@ -175,25 +160,28 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
         for (int e = 0; e < VEC; ++e) acc[r][e] = 0.f;
     }
 
-    // Byte offset of token tt of block `blk` (id: its pool block, paged mode).
+    // Byte offset of token tt of block `blk` (id: its pool block when paged).
+    // Paged: the block's base is uniform and the lane part fits 32 bits.
+    const int64_t col_stride = (int64_t)p.cols * tok_stride;    // ring: bytes per store row
     auto tok_addr = [&](int32_t blk, int32_t id, int tt) -> int64_t {
-        if (!paged) {
+        if constexpr (PAGED) {
+            return (int64_t)id * (16 * tok_stride) + head_off + (int32_t)(tt * (int32_t)tok_stride);
+        } else {
             int32_t r = (blk * 16) % p.rows + tt;
             if (r >= p.rows) r -= p.rows;
             if (r >= p.rows) r %= p.rows;       // rings shorter than a block
-            return ((int64_t)r * p.cols + ui.col) * tok_stride + head_off;
+            return (int64_t)r * col_stride + (int64_t)ui.col * tok_stride + head_off;
         }
-        return ((int64_t)id * 16 + tt) * tok_stride + head_off;
     };
     auto block_id = [&](int i) -> int32_t {
-        if (!paged) return 0;
+        if constexpr (!PAGED) return 0;
         if ((i & 63) == 0 && i > 0) {           // gather the next 64 ids
             const int32_t blk = first + kWaves * (i + lane);
             ids = blk < se ? p.block_table[(int64_t)u * p.max_blocks + blk] : -1;
         }
         return __builtin_amdgcn_readlane(ids, i & 63);
     };
-    auto id_ok = [&](int32_t id) { return !paged || (id >= 0 && id < p.num_blocks); };
+    auto id_ok = [&](int32_t id) { return !PAGED || (id >= 0 && id < p.num_blocks); };
 
     auto load = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
         const int32_t blk = first + kWaves * i;
@@ -555,7 +543,11 @@ bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group) {
 template <typename T, int D, int GT>
 static hipError_t launch_vec_t(const AttnParams& p, hipStream_t stream) {
     dim3 grid(p.num_splits, p.kv_heads, p.num_units);
-    attn_vec_kernel<T, D, GT><<<grid, dim3(kThreads), 0, stream>>>(p);
+    if (p.mode == kColumn) {
+        attn_vec_kernel<T, D, GT, false><<<grid, dim3(kThreads), 0, stream>>>(p);
+    } else {
+        attn_vec_kernel<T, D, GT, true><<<grid, dim3(kThreads), 0, stream>>>(p);
+    }
     return hipGetLastError();
 }
 

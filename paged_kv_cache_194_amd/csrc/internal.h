@@ -30,6 +30,11 @@ struct AttnParams {
     float* ws_o;           // split-K partial outputs [units*Hkv*splits][GT][D]
     float* ws_ml;          // split-K partial (max, sum) [units*Hkv*splits][GT][2]
     int32_t* ws_ticket;    // per (unit, kv head) arrival counters, zero between calls
+    float* mws_o;          // matrix-core path partials [units*Hkv*tiles*splits][BM][D]
+    float* mws_ml;         // and their (max, sum) [..][BM][2]
+    int32_t* mws_ticket;   // per (unit, kv head, tile) arrival counters
+    int32_t mfma_tiles;    // row tiles per (unit, kv head) on the matrix-core path
+    int32_t mfma_splits;
     int32_t mode;
     int32_t total_q;
     int32_t num_units;
@@ -45,8 +50,6 @@ struct AttnParams {
     int32_t causal;
     int32_t window;
     int32_t num_splits;
-    int32_t static_split;  // 1: split ranges cut from [0, nblk_cap) (no window, paged)
-    int32_t nblk_cap;      // ceil(kv_cap / 16)
     float scale_log2;      // softmax_scale * log2(e)
 };
 
@@ -95,6 +98,13 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
 hipError_t launch_attn_vec(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
                            hipStream_t stream);
 bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group);
+
+// Matrix-core path for units with several query rows (or a group > 8): bf16.
+hipError_t launch_attn_mfma(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
+                            hipStream_t stream);
+bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim);
+int32_t mfma_rows_per_group(int32_t head_dim);
+int32_t mfma_chunk_keys(int32_t head_dim);
 
 // Zero every output row of [0, total_q) that no unit covers.
 hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,

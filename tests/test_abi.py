@@ -77,7 +77,9 @@ def _decode(**over):
     (dict(B=-1), EINVAL),
     (dict(nb=0), EINVAL),
     (dict(splits=-2), EINVAL),
-    (dict(hq=32, hkv=2), EUNSUP),            # group 16 in decode
+    (dict(hq=32, hkv=2, dtype=F32), EUNSUP), # group 16 runs on the bf16 matrix-core path only
+    (dict(hq=32, hkv=2, kn=ctypes.c_void_p(16), vn=ctypes.c_void_p(16)), EUNSUP),  # no fused append there
+    (dict(hq=32, hkv=2), EINVAL),            # supported shape: null pointers are next
     (dict(kn=ctypes.c_void_p(16)), EINVAL),  # k_new without v_new
     (dict(scale=float("nan")), EINVAL),
 ])
@@ -125,6 +127,7 @@ def test_varlen_host_errors():
     assert _varlen(bt=p, cu=p, used=p, mq=0) == EINVAL
     assert _varlen(bt=p, cu=p, used=p, bs=8) == EINVAL
     assert _varlen(bt=p, cu=None, used=p) == EINVAL
+    assert _varlen(bt=p, cu=p, used=p, mq=4, dtype=F32) == EUNSUP   # multi-row fp32: no kernel
 
 
 def test_kv_append_host_errors():
