@@ -264,6 +264,8 @@ def bench_single_call(args, torch):
                                   num_splits=splits, workspace=ws)
         name = "long-context decode, 4 sequences 32K/64K, 64 q / 8 kv heads, D 256, 16 splits"
         extra = {}
+    elif args.config in ("c4", "c5"):
+        return bench_multirow(args, torch)
     else:
         raise SystemExit(f"unknown --config {args.config}")
     g = capture(torch, call)
@@ -279,12 +281,93 @@ def bench_single_call(args, torch):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
 
 
+def visible_pairs(E: int, L: int, causal: bool, window: int):
+    """(union of visible keys, number of visible (query, key) pairs) of one unit."""
+    lo_u, hi_u, pairs = None, 0, 0
+    for i in range(L):
+        p = E - L + i
+        hi = min(E, p + 1) if causal else E
+        lo = max(0, p - window + 1) if window > 0 else 0
+        if hi > lo:
+            pairs += hi - lo
+            lo_u = lo if lo_u is None else min(lo_u, lo)
+            hi_u = max(hi_u, hi)
+    return (0 if lo_u is None else hi_u - lo_u), pairs
+
+
+def bench_multirow(args, torch):
+    """Column store with decode + chunked-prefill segments (c4), or the
+    long-context draft-verify pass (c5): one attention call per step."""
+    import numpy as np
+
+    import paged_kv_cache_194_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    if args.config == "c4":
+        inp = workloads.c4_column(device=dev)
+        info = inp.seq_info.cpu().numpy()
+        units = [(int(r[1]), int(r[3])) for r in info]          # (L, E)
+        causal, window = True, 4096
+        mk = window + inp.max_seqlen_q - 1
+        out = torch.empty_like(inp.q)
+        ws = torch.zeros(max(1, pkv.attn_workspace_bytes(len(units), inp.max_seqlen_q, mk, inp.q_heads,
+                                                         inp.kv_heads, inp.head_dim, args.splits)),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            pkv.varlen_attn(out, inp.q, inp.k_store, inp.v_store, seq_info=inp.seq_info,
+                            max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=mk, softmax_scale=inp.scale,
+                            causal=True, window=window, num_splits=args.splits, workspace=ws)
+        name = "column store [8192,32,8,128]: 24 decode + 8 chunked-prefill segments, causal, window 4096"
+    else:
+        inp = workloads.c5_long(device=dev)
+        used = inp.seqused_k.cpu().numpy()
+        units = [(16, int(e)) for e in used]
+        causal, window = False, 0
+        out = torch.empty_like(inp.q)
+        ws = torch.zeros(max(1, pkv.attn_workspace_bytes(inp.num_seqs, inp.max_seqlen_q, inp.max_seqlen_k,
+                                                         inp.q_heads, inp.kv_heads, inp.head_dim, args.splits)),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            pkv.varlen_attn(out, inp.q, inp.k_cache, inp.v_cache, cu_seqlens_q=inp.cu_seqlens_q,
+                            seqused_k=inp.seqused_k, block_table=inp.block_table, max_seqlen_q=16,
+                            max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale, causal=False,
+                            num_splits=args.splits, workspace=ws)
+        name = "long-context draft verify: 4 x 16-token blocks over 32K/64K keys, 64 q / 8 kv heads, D 256"
+    keys = pairs = 0
+    for L, E in units:
+        k_u, p_u = visible_pairs(E, L, causal, window)
+        keys += k_u
+        pairs += p_u
+    kv_bytes = keys * inp.kv_heads * inp.head_dim * 2 * 2
+    flops = 4 * inp.head_dim * inp.q_heads * pairs
+    g = capture(torch, call)
+    time_graph(torch, g, max(1, args.warmup))
+    sec = time_graph(torch, g, args.steps)
+    gbs, tfs = kv_bytes / sec / 1e9, flops / sec / 1e12
+    hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tfs / 2500.0
+    bound = "hbm" if kv_bytes / (HBM_PEAK_GBS * 1e9) >= flops / 2.5e15 else "mfma"
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(hbm_frac, 4), "traffic": None} if bound == "hbm" else
+            {"bound": "mfma", "achieved": round(tfs, 2), "peak": 2500.0, "unit": "TFLOP/s",
+             "frac": round(mfma_frac, 4), "traffic": None})
+    return {"metric": f"{name}: KV GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+            "us_per_call": round(sec * 1e6, 2), "pct_hbm_peak": round(100 * hbm_frac, 2),
+            "tflops": round(tfs, 2), "pct_mfma_peak": round(100 * mfma_frac, 2),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": {"workload": name, "kv_bytes": kv_bytes, "flops": flops},
+            "roofline": roof}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c5d"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c5d"])
     ap.add_argument("--ctx", type=int, default=4096, help="live keys of the 42-layer decode step")
     ap.add_argument("--splits", type=int, default=0, help="split-K partitions (0: library choice)")
     ap.add_argument("--cpu-layers", type=int, default=42, help="layers the CPU oracle times")
