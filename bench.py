@@ -135,19 +135,39 @@ def bench_decode_step(args, torch):
     out = torch.zeros(m.layers, m.q_heads, m.head_dim, dtype=m.dtype, device=dev)
     runner = DecodeStepGraph(cache, inputs, out)
 
-    for _ in range(max(1, args.warmup)):
-        runner.step()
-    torch.cuda.synchronize()
-    graph = runner._graphs[(cache.bucket, cache.generation)]
-    t_wall0 = time.perf_counter()
-    sec_step = time_graph(torch, graph, args.steps)
-    wall = time.perf_counter() - t_wall0
+    if args.eager:
+        # plain launches, one step at a time (hardware counters are taken per dispatch)
+        for _ in range(max(1, args.warmup)):
+            runner.forward()
+        torch.cuda.synchronize()
+        t_wall0 = time.perf_counter()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.steps):
+            runner.forward()
+        e.record()
+        torch.cuda.synchronize()
+        sec_step = s.elapsed_time(e) / 1e3 / args.steps
+        wall = time.perf_counter() - t_wall0
+    else:
+        for _ in range(max(1, args.warmup)):
+            runner.step()
+        torch.cuda.synchronize()
+        graph = runner._graphs[(cache.bucket, cache.generation)]
+        t_wall0 = time.perf_counter()
+        sec_step = time_graph(torch, graph, args.steps)
+        wall = time.perf_counter() - t_wall0
 
     kv_bytes_layer = 2 * L * m.kv_heads * m.head_dim * 2
     kv_bytes_step = m.layers * kv_bytes_layer
 
     # Dominant kernel: the per-layer attention call, 42 back-to-back in a graph.
     ws = cache.workspace
+    if args.eager:
+        result_eager = {"metric": METRIC, "eager_us_per_step": round(sec_step * 1e6, 2), "wall_s": round(wall, 3)}
+        if args.copy_ceiling:
+            result_eager["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
+        return result_eager
 
     def attn_only():
         for i in range(m.layers):
@@ -373,6 +393,8 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=42, help="layers the CPU oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ceiling", action="store_true", help="also time a 4 GiB device copy")
+    ap.add_argument("--eager", action="store_true",
+                    help="c2 only: plain launches instead of graph replays (for per-dispatch counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))

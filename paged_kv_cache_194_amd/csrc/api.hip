@@ -55,12 +55,12 @@ int32_t clamp_splits(int64_t s, int64_t cap) {
     return (int32_t)(s < 1 ? 1 : s);
 }
 
-// Vector path: about 2048 work groups, at least 4 blocks (one per wave) each.
+// Vector path: about 2048 work groups, at least 8 blocks (two per wave) each.
 int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_splits) {
     if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
     const int64_t base = (int64_t)(units > 0 ? units : 1) * kv_heads;
     const int64_t blocks = ((int64_t)(keys > 0 ? keys : 1) + 15) / 16;
-    return clamp_splits((2048 + base - 1) / base, blocks / 4 > 0 ? blocks / 4 : 1);
+    return clamp_splits((2048 + base - 1) / base, blocks / 8 > 0 ? blocks / 8 : 1);
 }
 
 // Plan of one attention call: which paths run, their split counts and the
