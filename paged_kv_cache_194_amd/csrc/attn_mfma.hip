@@ -59,6 +59,12 @@ struct MfmaCfg {
     static constexpr int KT = BN / 16;            // 16-key tiles per chunk
     static constexpr int KS = D / 32;             // k-steps of the QK product
     static constexpr int DT = D / 16;             // 16-wide d tiles of O
+    // V^T rows hold BN/2 key pairs (one dword each).  The pair column is
+    // XOR-swizzled by the row's 8-row group (an even amount, so the two pairs a
+    // PV operand reads stay adjacent): staging writes from lanes 8 rows apart
+    // then land in different banks.
+    static constexpr int SWZ_MASK = (BN / 2 - 1) & ~1;
+    __device__ static int vcol(int d, int pair) { return pair ^ ((2 * (d >> 3)) & SWZ_MASK); }
     static_assert(KITEMS % NT == 0 && VITEMS % NT == 0, "chunk must split evenly over threads");
     static_assert(BN % 32 == 0, "PV k-steps take 32 keys");
 };
@@ -201,8 +207,8 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
             for (int w = 0; w < 4; ++w) {
                 const uint32_t a = word(vreg[k][0], w), b = word(vreg[k][1], w);
                 const int d = part * 8 + 2 * w;
-                *reinterpret_cast<uint32_t*>(sV + d * VST + (2 * kp) * 2) = pair_lo(a, b);
-                *reinterpret_cast<uint32_t*>(sV + (d + 1) * VST + (2 * kp) * 2) = pair_hi(a, b);
+                *reinterpret_cast<uint32_t*>(sV + d * VST + C::vcol(d, kp) * 4) = pair_lo(a, b);
+                *reinterpret_cast<uint32_t*>(sV + (d + 1) * VST + C::vcol(d + 1, kp) * 4) = pair_hi(a, b);
             }
         }
     };
@@ -292,9 +298,10 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
             const int kk0 = s2 * 32 + 4 * lq;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const uint8_t* vrow = sV + (dt * 16 + lr) * VST;
-                const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + kk0 * 2);
-                const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + (kk0 + 16) * 2);
+                const int d = dt * 16 + lr;
+                const uint8_t* vrow = sV + d * VST;
+                const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + C::vcol(d, kk0 / 2) * 4);
+                const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + C::vcol(d, (kk0 + 16) / 2) * 4);
                 o[dt] = mfma16(u32x4{lo4.x, lo4.y, hi4.x, hi4.y}, b, o[dt]);
             }
         }

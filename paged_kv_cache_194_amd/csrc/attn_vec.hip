@@ -78,6 +78,59 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     }
 }
 
+// Merge of the S split partials of one (unit, kv head): each thread takes 4
+// consecutive outputs of one head, 32 splits' (m, l, o) in flight at a time
+// (indices past S are clamped and weighted 0), with a running max across chunks.
+template <typename T, int D, int GT>
+__device__ __forceinline__ void merge_splits(const AttnParams& p, int32_t u, int32_t g, int32_t row) {
+    const int32_t S = p.num_splits, G = p.group, Hkv = p.kv_heads;
+    const int64_t w0 = ((int64_t)u * Hkv + g) * S;
+    constexpr int CH = 32;
+    for (int idx = threadIdx.x; idx < GT * (D / 4); idx += blockDim.x) {
+        const int r = idx / (D / 4), d4 = (idx - r * (D / 4)) * 4;
+        if (r >= G) continue;
+        const float* osrc = p.ws_o + (w0 * GT + r) * D + d4;
+        const float* msrc = p.ws_ml + (w0 * GT + r) * 2;
+        const int64_t ostride = (int64_t)GT * D, mstride = (int64_t)GT * 2;
+        float M = -INFINITY, tot = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < S; s0 += CH) {
+            float2 ml[CH];
+            float4 x[CH];
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const int sk = min(s0 + k, S - 1);
+                ml[k] = *reinterpret_cast<const float2*>(msrc + sk * mstride);
+                x[k] = *reinterpret_cast<const float4*>(osrc + sk * ostride);
+            }
+            float Mc = M;
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+                if (s0 + k < S) Mc = fmaxf(Mc, ml[k].x);
+            if (Mc == -INFINITY) continue;      // nothing visible yet
+            const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mc);
+            tot *= a;
+            o.x *= a; o.y *= a; o.z *= a; o.w *= a;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const float w = (s0 + k < S && ml[k].x != -INFINITY) ? fast_exp2(ml[k].x - Mc) : 0.f;
+                tot = fmaf(w, ml[k].y, tot);
+                o.x = fmaf(w, x[k].x, o.x);
+                o.y = fmaf(w, x[k].y, o.y);
+                o.z = fmaf(w, x[k].z, o.z);
+                o.w = fmaf(w, x[k].w, o.w);
+            }
+            M = Mc;
+        }
+        const float inv = tot > 0.f ? 1.f / tot : 0.f;
+        const int64_t oi = ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d4;
+        store_out<T>(p.out, oi + 0, o.x * inv);
+        store_out<T>(p.out, oi + 1, o.y * inv);
+        store_out<T>(p.out, oi + 2, o.z * inv);
+        store_out<T>(p.out, oi + 3, o.w * inv);
+    }
+}
+
 template <typename T, int D, int GT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     using C = VecCfg<T, D, GT>;
@@ -452,54 +505,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (threadIdx.x == 0)                       // ready for the next call
         __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Each thread merges 4 consecutive outputs of one head over all splits, 16
-    // splits' (m, l, o) in flight at a time (indices past S are clamped and
-    // weighted 0), with a running max across chunks.
-    const int64_t w0 = ((int64_t)u * Hkv + g) * S;
-    constexpr int CH = 32;
-    for (int idx = threadIdx.x; idx < GT * (D / 4); idx += kThreads) {
-        const int r = idx / (D / 4), d4 = (idx - r * (D / 4)) * 4;
-        if (r >= G) continue;
-        const float* osrc = p.ws_o + (w0 * GT + r) * D + d4;
-        const float* msrc = p.ws_ml + (w0 * GT + r) * 2;
-        const int64_t ostride = (int64_t)GT * D, mstride = (int64_t)GT * 2;
-        float M = -INFINITY, tot = 0.f;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s0 = 0; s0 < S; s0 += CH) {
-            float2 ml[CH];
-            float4 x[CH];
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                const int sk = min(s0 + k, S - 1);
-                ml[k] = *reinterpret_cast<const float2*>(msrc + sk * mstride);
-                x[k] = *reinterpret_cast<const float4*>(osrc + sk * ostride);
-            }
-            float Mc = M;
-#pragma unroll
-            for (int k = 0; k < CH; ++k)
-                if (s0 + k < S) Mc = fmaxf(Mc, ml[k].x);
-            if (Mc == -INFINITY) continue;      // nothing visible yet
-            const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mc);
-            tot *= a;
-            o.x *= a; o.y *= a; o.z *= a; o.w *= a;
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                const float w = (s0 + k < S && ml[k].x != -INFINITY) ? fast_exp2(ml[k].x - Mc) : 0.f;
-                tot = fmaf(w, ml[k].y, tot);
-                o.x = fmaf(w, x[k].x, o.x);
-                o.y = fmaf(w, x[k].y, o.y);
-                o.z = fmaf(w, x[k].z, o.z);
-                o.w = fmaf(w, x[k].w, o.w);
-            }
-            M = Mc;
-        }
-        const float inv = tot > 0.f ? 1.f / tot : 0.f;
-        const int64_t oi = ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d4;
-        store_out<T>(p.out, oi + 0, o.x * inv);
-        store_out<T>(p.out, oi + 1, o.y * inv);
-        store_out<T>(p.out, oi + 2, o.z * inv);
-        store_out<T>(p.out, oi + 3, o.w * inv);
-    }
+    merge_splits<T, D, GT>(p, u, g, row);
 }
 
 // Zero the output rows that no unit covers.
