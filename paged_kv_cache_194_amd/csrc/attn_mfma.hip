@@ -332,16 +332,14 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
     const int rloc = wave * 16 + lr;
     float* po = p.mws_o + (wi * BM + rloc) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st_agent(po + dt * 16 + 4 * lq + e, o[dt][e]);
-    if (lq == 0) {
-        st_agent(&p.mws_ml[(wi * BM + rloc) * 2 + 0], m_run);
-        st_agent(&p.mws_ml[(wi * BM + rloc) * 2 + 1], l_run);
+    for (int dt = 0; dt < DT; ++dt) {
+        st_agent2(po + dt * 16 + 4 * lq, o[dt][0], o[dt][1]);
+        st_agent2(po + dt * 16 + 4 * lq + 2, o[dt][2], o[dt][3]);
     }
+    if (lq == 0) st_agent2(&p.mws_ml[(wi * BM + rloc) * 2], m_run, l_run);
     wait_vm_all();
     __syncthreads();
-    int32_t* ticket = p.mws_ticket + (((int64_t)u * Hkv + g) * T + tile);
+    int32_t* ticket = p.mws_ticket + (((int64_t)u * Hkv + g) * T + tile) * kTicketStride;
     if (tid == 0)
         sLast = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1);
     __syncthreads();
@@ -372,17 +370,17 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
                 ml[k] = *reinterpret_cast<const float2*>(msrc + sk * mstride);
                 x[k] = *reinterpret_cast<const float4*>(osrc + sk * ostride);
             }
+            // No branch on loaded values, so all loads of a pass are in flight together.
             float Mc = Mx;
 #pragma unroll
-            for (int k = 0; k < CH; ++k)
-                if (s0 + k < S) Mc = fmaxf(Mc, ml[k].x);
-            if (Mc == -INFINITY) continue;
-            const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - Mc);
+            for (int k = 0; k < CH; ++k) Mc = (s0 + k < S) ? fmaxf(Mc, ml[k].x) : Mc;
+            const float Mu = (Mc == -INFINITY) ? 0.f : Mc;
+            const float a = fast_exp2(Mx - Mu);     // 0 while nothing was visible
             tot *= a;
             acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
-                const float w = (s0 + k < S && ml[k].x != -INFINITY) ? fast_exp2(ml[k].x - Mc) : 0.f;
+                const float w = (s0 + k < S) ? fast_exp2(ml[k].x - Mu) : 0.f;
                 tot = fmaf(w, ml[k].y, tot);
                 acc.x = fmaf(w, x[k].x, acc.x);
                 acc.y = fmaf(w, x[k].y, acc.y);

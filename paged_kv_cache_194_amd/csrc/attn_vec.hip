@@ -9,10 +9,9 @@
 // at position E-1, as PagedDecodeCache.attend does before attending.
 //
 // One kernel per call.  Work decomposition: one work group (4 waves) per
-// (split, kv head, unit).  The unit's keys, as whole 16-token blocks, are cut
-// into `splits` contiguous block ranges -- from the static bound [0, ceil(cap/16))
-// when there is no window (so the block-table gather needs no live length and
-// overlaps the seqused_k load), from the live range otherwise.  Wave w of a work
+// (split, kv head, unit).  The unit's visible keys, as whole 16-token blocks,
+// are cut into `splits` contiguous block ranges of the live range, so the work
+// per call follows the live length, not the bucket.  Wave w of a work
 // group takes blocks w, w+4, ... of its range: the reduction order depends only
 // on logical positions, so a permuted block table gives bit-identical results.
 // Each wave gathers the block ids of all its blocks with one vector load and
@@ -78,42 +77,64 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     }
 }
 
-// Merge of the S split partials of one (unit, kv head): each thread takes 4
-// consecutive outputs of one head, 32 splits' (m, l, o) in flight at a time
-// (indices past S are clamped and weighted 0), with a running max across chunks.
+// Log-sum-exp merge of this lane's (M, tot, o) with lane (lane ^ ST)'s.
+template <int ST>
+__device__ __forceinline__ void combine_lanes(float& M, float& tot, float4& o) {
+    const float Mo = xor_lanes<ST>(M), to = xor_lanes<ST>(tot);
+    const float ox = xor_lanes<ST>(o.x), oy = xor_lanes<ST>(o.y);
+    const float oz = xor_lanes<ST>(o.z), ow = xor_lanes<ST>(o.w);
+    const float Mn = fmaxf(M, Mo);
+    const float Mu = (Mn == -INFINITY) ? 0.f : Mn;
+    const float a = fast_exp2(M - Mu), b = fast_exp2(Mo - Mu);
+    tot = fmaf(a, tot, b * to);
+    o.x = fmaf(a, o.x, b * ox);
+    o.y = fmaf(a, o.y, b * oy);
+    o.z = fmaf(a, o.z, b * oz);
+    o.w = fmaf(a, o.w, b * ow);
+    M = Mn;
+}
+
+// Merge of the S split partials of one (unit, kv head).  NP consecutive lanes
+// share one group of 4 outputs of one head; lane part k of the group takes the
+// splits k, k + NP, ...  Every load of a pass is issued before any is used and
+// nothing branches on loaded values, so a pass costs one memory round trip.
+// Splits past S are clamped to S-1 and weighted 0; an empty split (m = -inf)
+// gets weight 0.  The NP lane results meet through lane swizzles.
 template <typename T, int D, int GT>
 __device__ __forceinline__ void merge_splits(const AttnParams& p, int32_t u, int32_t g, int32_t row) {
+    constexpr int ITEMS = GT * (D / 4);
+    constexpr int NP = ITEMS >= kThreads ? 1 : (kThreads / ITEMS > 16 ? 16 : kThreads / ITEMS);
+    constexpr int CH = NP == 1 ? 32 : NP == 2 ? 16 : 8;
     const int32_t S = p.num_splits, G = p.group, Hkv = p.kv_heads;
     const int64_t w0 = ((int64_t)u * Hkv + g) * S;
-    constexpr int CH = 32;
-    for (int idx = threadIdx.x; idx < GT * (D / 4); idx += blockDim.x) {
-        const int r = idx / (D / 4), d4 = (idx - r * (D / 4)) * 4;
-        if (r >= G) continue;
+    const int part = threadIdx.x % NP;
+    for (int item = threadIdx.x / NP; item < ITEMS; item += kThreads / NP) {
+        const int r = item / (D / 4), d4 = (item - r * (D / 4)) * 4;
+        if (r >= G) continue;                   // uniform over the NP lanes of an item
         const float* osrc = p.ws_o + (w0 * GT + r) * D + d4;
         const float* msrc = p.ws_ml + (w0 * GT + r) * 2;
         const int64_t ostride = (int64_t)GT * D, mstride = (int64_t)GT * 2;
         float M = -INFINITY, tot = 0.f;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s0 = 0; s0 < S; s0 += CH) {
+        for (int s0 = 0; s0 < S; s0 += NP * CH) {
             float2 ml[CH];
             float4 x[CH];
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
-                const int sk = min(s0 + k, S - 1);
+                const int sk = min(s0 + part + NP * k, S - 1);
                 ml[k] = *reinterpret_cast<const float2*>(msrc + sk * mstride);
                 x[k] = *reinterpret_cast<const float4*>(osrc + sk * ostride);
             }
             float Mc = M;
 #pragma unroll
-            for (int k = 0; k < CH; ++k)
-                if (s0 + k < S) Mc = fmaxf(Mc, ml[k].x);
-            if (Mc == -INFINITY) continue;      // nothing visible yet
-            const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mc);
+            for (int k = 0; k < CH; ++k) Mc = (s0 + part + NP * k < S) ? fmaxf(Mc, ml[k].x) : Mc;
+            const float Mu = (Mc == -INFINITY) ? 0.f : Mc;
+            const float a = fast_exp2(M - Mu);  // 0 while nothing was visible
             tot *= a;
             o.x *= a; o.y *= a; o.z *= a; o.w *= a;
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
-                const float w = (s0 + k < S && ml[k].x != -INFINITY) ? fast_exp2(ml[k].x - Mc) : 0.f;
+                const float w = (s0 + part + NP * k < S) ? fast_exp2(ml[k].x - Mu) : 0.f;
                 tot = fmaf(w, ml[k].y, tot);
                 o.x = fmaf(w, x[k].x, o.x);
                 o.y = fmaf(w, x[k].y, o.y);
@@ -122,6 +143,11 @@ __device__ __forceinline__ void merge_splits(const AttnParams& p, int32_t u, int
             }
             M = Mc;
         }
+        if constexpr (NP > 1) combine_lanes<1>(M, tot, o);
+        if constexpr (NP > 2) combine_lanes<2>(M, tot, o);
+        if constexpr (NP > 4) combine_lanes<4>(M, tot, o);
+        if constexpr (NP > 8) combine_lanes<8>(M, tot, o);
+        if (part != 0) continue;
         const float inv = tot > 0.f ? 1.f / tot : 0.f;
         const int64_t oi = ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d4;
         store_out<T>(p.out, oi + 0, o.x * inv);
@@ -456,48 +482,50 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     __syncthreads();
 
     const int64_t wi = ((int64_t)u * Hkv + g) * S + split;
-    for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
-        const int r = idx / D, d = idx - (idx / D) * D;
+    for (int idx = threadIdx.x; idx < GT * (D / 2); idx += kThreads) {
+        const int r = idx / (D / 2), d = (idx - r * (D / 2)) * 2;
         if (r >= G) continue;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sM[w][r]);
-        float o = 0.f, lsum = 0.f;
+        float o0 = 0.f, o1 = 0.f, lsum = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float sc = fast_exp2(sM[w][r] - M);
-                float ow = 0.f, lw = 0.f;
+                float ow0 = 0.f, ow1 = 0.f, lw = 0.f;
 #pragma unroll
                 for (int t = 0; t < VR; ++t) {
-                    ow += sAcc[w][t][r][d];
+                    const float2 a2 = *reinterpret_cast<const float2*>(&sAcc[w][t][r][d]);
+                    ow0 += a2.x;
+                    ow1 += a2.y;
                     lw += sLv[w][t][r];
                 }
-                o = fmaf(sc, ow, o);
+                o0 = fmaf(sc, ow0, o0);
+                o1 = fmaf(sc, ow1, o1);
                 lsum = fmaf(sc, lw, lsum);
             }
         }
         if (S == 1) {
-            store_out<T>(p.out, ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d,
-                         lsum > 0.f ? o / lsum : 0.f);
+            const int64_t oi = ((int64_t)row * p.q_heads + (int64_t)g * G + r) * D + d;
+            store_out<T>(p.out, oi, lsum > 0.f ? o0 / lsum : 0.f);
+            store_out<T>(p.out, oi + 1, lsum > 0.f ? o1 / lsum : 0.f);
         } else {
-            st_agent(&p.ws_o[(wi * GT + r) * D + d], o);
-            if (d == 0) {
-                st_agent(&p.ws_ml[(wi * GT + r) * 2 + 0], M);
-                st_agent(&p.ws_ml[(wi * GT + r) * 2 + 1], lsum);
-            }
+            st_agent2(&p.ws_o[(wi * GT + r) * D + d], o0, o1);
+            if (d == 0) st_agent2(&p.ws_ml[(wi * GT + r) * 2], M, lsum);
         }
     }
     if (S == 1) return;
 
     // ---- split-K: the last work group of this (unit, kv head) merges ----
-    // Partials went out with device-coherent stores; once every wave's stores
+    // Partials go out with device-coherent stores; once every wave's stores
     // have completed, one thread takes a ticket.  The work group drawing the
     // last ticket drops its stale cache lines (an agent-scope acquire: no
-    // writeback) and reads all partials with 16-byte loads.
+    // writeback) and reads all partials with 16-byte loads (one round trip;
+    // device-coherent 8-byte loads instead measured slower).
     wait_vm_all();
     __syncthreads();
-    int32_t* ticket = p.ws_ticket + ((int64_t)u * Hkv + g);
+    int32_t* ticket = p.ws_ticket + ((int64_t)u * Hkv + g) * kTicketStride;
     if (threadIdx.x == 0)
         sLast = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1);
     __syncthreads();
@@ -537,7 +565,7 @@ int32_t vec_group_rows(int32_t group) {
 }
 
 size_t ticket_bytes(int32_t units, int32_t kv_heads) {
-    const size_t n = (size_t)units * kv_heads * sizeof(int32_t);
+    const size_t n = (size_t)units * kv_heads * kTicketStride * sizeof(int32_t);
     return (n + 255) / 256 * 256;
 }
 

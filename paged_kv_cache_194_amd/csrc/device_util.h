@@ -119,15 +119,15 @@ __device__ __forceinline__ float across_groups(float x) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Device-coherent (agent scope) word access.  On gfx950 these are plain loads
-// and stores with the sc1 scope bit: they bypass the per-XCD L2's
-// non-coherent lines without the whole-cache writeback/invalidate that a
-// device-scope fence costs.  Used to hand split-K partials between work groups.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Two adjacent floats (8-byte aligned) as one device-coherent (agent scope)
+// 64-bit store.  On gfx950 this is a plain store with the sc1 scope bit: it
+// reaches the coherence point past the per-XCD L2 without the whole-cache
+// writeback that a device-scope fence costs.  Used to hand split-K partials
+// between work groups.
+__device__ __forceinline__ void st_agent2(float* p, float a, float b) {
+    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, a) |
+                       ((uint64_t)__builtin_bit_cast(uint32_t, b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every vector memory access this wave issued has completed.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }

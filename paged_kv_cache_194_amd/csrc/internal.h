@@ -113,6 +113,10 @@ hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t h
 // Rows of query a vector-path work group holds (group size rounded up).
 int32_t vec_group_rows(int32_t group);
 
+// Arrival counters of split-K sit one per 256 bytes, so that the work groups
+// of different heads do not queue on one memory line.
+constexpr int32_t kTicketStride = 64;
+
 // Bytes of the arrival counters at the start of a split-K workspace.
 size_t ticket_bytes(int32_t units, int32_t kv_heads);
 
