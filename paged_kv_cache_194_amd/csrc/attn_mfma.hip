@@ -14,13 +14,16 @@
 // for a kv head is used by all of its query heads.  A work group (NW waves)
 // takes BM = 16*NW of those rows and a range of 64-key chunks.
 //
-// Per chunk the work group stages K row-major and V transposed ([d][key]) in
-// LDS -- keys outside the rows' union of visible ranges, or without storage,
-// are staged as zeros -- and each wave runs two bf16 MFMA passes for its 16
-// rows with v_mfma_f32_16x16x32_bf16:
+// Per chunk the work group stages K and V row-major in LDS -- keys outside
+// the rows' union of visible ranges, or without storage, are staged as zeros --
+// and each wave runs two bf16 MFMA passes for its 16 rows with
+// v_mfma_f32_16x16x32_bf16:
 //   S^T[key][row] = K . Q^T     (A = K from LDS, B = Q^T from registers)
-//   O^T[d][row]  += V^T . P^T   (A = V^T from LDS, B = P^T straight from the
+//   O^T[d][row]  += V^T . P^T   (A = V^T built by transposing LDS reads,
+//                                ds_read_b64_tr_b16; B = P^T straight from the
 //                                C layout of S^T)
+// Chunks come from global memory through a ring of register slots, several
+// chunks ahead of the one being computed, into two LDS buffers.
 // Working transposed puts one query row per lane column, so the online-softmax
 // statistics and the rescale of O stay inside the lane (plus a 4-lane-group
 // max/sum).  The k order of the second product is the key permutation the
@@ -43,40 +46,96 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4& a, const u32x4& b, f32x4_
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
+// of the 8-byte chunks named by lanes 4m + i / 4, m = 0..3 (a 4 x 4 transpose
+// of 16-bit elements per group).
+__device__ __forceinline__ v4i16 ds_read_tr16(const uint8_t* lds) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(lds));
+}
+__device__ __forceinline__ uint32_t pair_bits(const v4i16& v, int h) {
+    return (uint32_t)(uint16_t)v[2 * h] | ((uint32_t)(uint16_t)v[2 * h + 1] << 16);
+}
+
 constexpr int kIdWindow = 1024;   // block ids staged in LDS at a time
 
-template <int D, int NW, int BN>
+
+// Direct-to-LDS 16-byte load (global_load_lds_dwordx4): lane i's 16 bytes from
+// `src` land at LDS byte address lds + 16*i (lds wave-uniform, through M0).
+// Issued from inline assembly so that the compiler's wait-count bookkeeping
+// does not serialize it; the kernel places its own waits.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+// Wait until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// Source of the bytes staged for a key that is not wanted or has no storage.
+__device__ __attribute__((aligned(16))) uint8_t kZeroRow[512];
+
+// Launch shape per head_dim: NW waves, each owning RT tiles of 16 query rows
+// (every K/V fragment a wave reads from LDS feeds RT MFMAs), chunks of BN
+// keys, NS LDS stages (NS - 1 chunks in flight while one is computed), at
+// least WPE waves per SIMD (a register cap).  Measured on the chunked-prefill
+// and draft-verify workloads: with two row tiles a D = 128 wave fits two to a
+// SIMD and two 68 KiB work groups share a CU; at D = 256 two row tiles do not
+// fit two waves to a SIMD, and eight one-tile waves with four stages win.
+template <int D>
+struct MfmaShape;
+template <>
+struct MfmaShape<64> { static constexpr int NW = 4, RT = 2, BN = 64, NS = 4, WPE = 2; };
+template <>
+struct MfmaShape<128> { static constexpr int NW = 4, RT = 2, BN = 64, NS = 2, WPE = 2; };
+template <>
+struct MfmaShape<256> { static constexpr int NW = 8, RT = 1, BN = 32, NS = 4, WPE = 1; };
+
+template <int D, int NW, int RT, int BN, int NS>
 struct MfmaCfg {
     static constexpr int NT = 64 * NW;            // threads
-    static constexpr int BM = 16 * NW;            // query rows per work group
-    static constexpr int KST = D * 2 + 16;        // LDS bytes per staged K row
-    static constexpr int VST = BN * 2 + 16;       // LDS bytes per staged V^T row
-    static constexpr int DP = D / 8;              // 16-byte parts per key row
-    static constexpr int KITEMS = BN * DP;        // K chunk: 16-byte items
-    static constexpr int VITEMS = (BN / 2) * DP;  // V chunk: key-pair items
-    static constexpr int KPT = (KITEMS + NT - 1) / NT;
-    static constexpr int VPT = (VITEMS + NT - 1) / NT;
+    static constexpr int BM = 16 * NW * RT;       // query rows per work group
+    static constexpr int RB = D * 2;              // bytes per key row (one head)
+    static constexpr int RC = D / 8;              // 16-byte columns per row
+    static constexpr int CB = BN * RB;            // bytes of one chunk of K (or V)
+    static constexpr int NI = CB / 1024;          // 1 KiB wave loads per chunk of K (or V)
+    static constexpr int IPW = NI / NW;           // ... per wave
     static constexpr int KT = BN / 16;            // 16-key tiles per chunk
     static constexpr int KS = D / 32;             // k-steps of the QK product
     static constexpr int DT = D / 16;             // 16-wide d tiles of O
-    // V^T rows hold BN/2 key pairs (one dword each).  The pair column is
-    // XOR-swizzled by the row's 8-row group (an even amount, so the two pairs a
-    // PV operand reads stay adjacent): staging writes from lanes 8 rows apart
-    // then land in different banks.
-    static constexpr int SWZ_MASK = (BN / 2 - 1) & ~1;
-    __device__ static int vcol(int d, int pair) { return pair ^ ((2 * (d >> 3)) & SWZ_MASK); }
-    static_assert(KITEMS % NT == 0 && VITEMS % NT == 0, "chunk must split evenly over threads");
+    static_assert(NI % NW == 0 && IPW >= 1, "chunk must split evenly over waves");
     static_assert(BN % 32 == 0, "PV k-steps take 32 keys");
+    static_assert(RB <= 512, "zero row covers one key row");
+    // Rows are stored unpadded with their 16-byte columns permuted by the row:
+    // XOR with 2*row inside each group of 16 columns (D >= 128), rotation by
+    // the row within the 8 columns (D = 64).  Measured on gfx950 with the
+    // kernel's two read patterns (16-row ds_read_b128 for K, ds_read_b64_tr_b16
+    // for V), either leaves no LDS bank conflicts.  swz maps a logical column
+    // to its stored place; unswz is the inverse.
+    __device__ static int swz(int r, int c) {
+        if constexpr (RC >= 16) return c ^ ((2 * r) & 15);
+        else return (c + r) & (RC - 1);
+    }
+    __device__ static int unswz(int r, int c) {
+        if constexpr (RC >= 16) return c ^ ((2 * r) & 15);
+        else return (c - r) & (RC - 1);
+    }
 };
 
-template <int D, int NW, int BN, bool PAGED>
-__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
-    using C = MfmaCfg<D, NW, BN>;
-    constexpr int NT = C::NT, BM = C::BM, KST = C::KST, VST = C::VST, DP = C::DP, KPT = C::KPT,
-                  VPT = C::VPT, KT = C::KT, KS = C::KS, DT = C::DT;
+template <int D, int NW, int RT, int BN, int NS, int WPE, bool PAGED>
+__global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
+    using C = MfmaCfg<D, NW, RT, BN, NS>;
+    constexpr int NT = C::NT, BM = C::BM, RB = C::RB, RC = C::RC, CB = C::CB, IPW = C::IPW,
+                  KT = C::KT, KS = C::KS, DT = C::DT;
 
-    __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
-    __shared__ __attribute__((aligned(16))) uint8_t sV[D * VST];
+    // Stage s holds one chunk: K rows at sKV[s][0], V rows at sKV[s][CB].
+    __shared__ __attribute__((aligned(1024))) uint8_t sKV[NS][2 * CB];
     __shared__ int32_t sIds[kIdWindow];
     __shared__ int32_t sLast;
 
@@ -105,13 +164,13 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
     const int32_t Hkv = p.kv_heads;
 
     // Visible range of position i (row i of the unit).
-    auto lo_of = [&](int32_t i) -> int32_t {
+    auto lo_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t {
         if (p.window <= 0) return 0;
         const int32_t pos = E - L + i;
         const int32_t lo = pos - p.window + 1;
         return lo > 0 ? lo : 0;
     };
-    auto hi_of = [&](int32_t i) -> int32_t {
+    auto hi_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t {
         if (!p.causal) return E;
         const int32_t pos1 = E - L + i + 1;
         return pos1 < E ? (pos1 > 0 ? pos1 : 0) : E;
@@ -126,29 +185,38 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
     const int32_t c_first = split * cps;
     const int32_t c_end = min(nchunk, c_first + cps);
 
-    // This lane's row.
-    const int32_t my_m = m0 + wave * 16 + lr;
-    const bool row_ok = my_m < M;
-    const int32_t my_i = row_ok ? my_m / G : 0;
-    const int32_t my_h = row_ok ? my_m - my_i * G : 0;
-    const int32_t my_lo = lo_of(my_i), my_hi = row_ok ? hi_of(my_i) : 0;
-
-    const bool in_rows = row_ok && (ui.q_start + my_i) >= 0 && (ui.q_start + my_i) < p.total_q;
-
-    // Q^T operand: row my_m, d = ks*32 + 8*lq .. +7.
-    u32x4 qf[KS];
-    {
+    // This lane's rows: row lr of the wave's tiles rt = 0 .. RT-1.
+    int32_t my_i[RT], my_h[RT], my_lo[RT], my_hi[RT];
+    bool in_rows[RT];
+    u32x4 qf[RT][KS];                             // Q^T operand: d = ks*32 + 8*lq .. +7
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int32_t mm = m0 + (wave * RT + rt) * 16 + lr;
+        const bool row_ok = mm < M;
+        my_i[rt] = row_ok ? mm / G : 0;
+        my_h[rt] = row_ok ? mm - my_i[rt] * G : 0;
+        my_lo[rt] = lo_of(my_i[rt]);
+        my_hi[rt] = row_ok ? hi_of(my_i[rt]) : 0;
+        in_rows[rt] = row_ok && (ui.q_start + my_i[rt]) >= 0 && (ui.q_start + my_i[rt]) < p.total_q;
         const uint8_t* qb = (const uint8_t*)p.q +
-                            (((int64_t)(ui.q_start + my_i) * p.q_heads + (int64_t)g * G + my_h) * D) * 2;
+                            (((int64_t)(ui.q_start + my_i[rt]) * p.q_heads + (int64_t)g * G + my_h[rt]) * D) * 2;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qf[ks] = in_rows ? ld16(qb + (ks * 32 + 8 * lq) * 2) : u32x4{0u, 0u, 0u, 0u};
+            qf[rt][ks] = in_rows[rt] ? ld16(qb + (ks * 32 + 8 * lq) * 2) : u32x4{0u, 0u, 0u, 0u};
     }
+    // Q complete before the pipeline starts: otherwise the first use of qf in the
+    // chunk loop would wait for every load in flight.
+    wait_vm_all();
 
-    f32x4_t o[DT];
+    f32x4_t o[RT][DT];
+    float m_run[RT], l_run[RT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run[rt] = -INFINITY;
+        l_run[rt] = 0.f;
+    }
 
     const uint8_t* __restrict__ Kg = (const uint8_t*)p.k;
     const uint8_t* __restrict__ Vg = (const uint8_t*)p.v;
@@ -156,64 +224,46 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
     const int64_t head_off = (int64_t)g * D * 2;
     int32_t id_base = -kIdWindow;                 // first block of the staged id window
 
-    // Byte offset of key j (head g) in K or V, or -1 when it has no storage.
-    auto key_addr = [&](int32_t j) -> int64_t {
+    // Byte offset of key j (head g) in K or V, or -1 when the key is not
+    // wanted (`want` false) or has no storage.  Branch-free: the id window is
+    // read at a clamped index and the checks are selects.
+    auto key_addr = [&](int32_t j, bool want) __attribute__((always_inline)) -> int64_t {
         if constexpr (PAGED) {
-            const int32_t id = sIds[(j >> 4) - id_base];
-            if (id < 0 || id >= p.num_blocks) return -1;
-            return ((int64_t)id * 16 + (j & 15)) * tok_stride + head_off;
+            int32_t w = (j >> 4) - id_base;
+            w = w < 0 ? 0 : (w >= kIdWindow ? kIdWindow - 1 : w);
+            const int32_t id = sIds[w];
+            const bool ok = want && id >= 0 && id < p.num_blocks;
+            return ok ? ((int64_t)id * 16 + (j & 15)) * tok_stride + head_off : -1;
         } else {
-            int32_t r = j % p.rows;
-            return ((int64_t)r * p.cols + ui.col) * tok_stride + head_off;
+            const int32_t r = (j >= 0 ? j : 0) % p.rows;
+            return want ? ((int64_t)r * p.cols + ui.col) * tok_stride + head_off : -1;
         }
     };
 
-    // Registers carrying the next chunk from global memory to LDS.
-    u32x4 kreg[KPT], vreg[VPT][2];
-    auto fetch = [&](int32_t c) {
+    // Issue chunk c (of this work group's range; past c_end nothing is wanted)
+    // into stage st: wave loads w, w + NW, ... of K and of V.  Lane i of wave
+    // load I fills stored place I*64 + i of the chunk: row r, stored column cs,
+    // which holds logical column unswz(r, cs) of key c0 + r.
+    auto issue = [&](int32_t c, int st) __attribute__((always_inline)) {
         const int32_t c0 = c_base + c * BN;
+        const bool chunk_ok = c < c_end;
+        const uint32_t kdst = lds_addr(&sKV[st][0]), vdst = lds_addr(&sKV[st][CB]);
 #pragma unroll
-        for (int k = 0; k < KPT; ++k) {
-            const int ci = tid + k * NT;
-            const int kk = ci / DP, part = ci - (ci / DP) * DP;
-            const int32_t j = c0 + kk;
-            int64_t a = (j >= key_lo && j < key_hi) ? key_addr(j) : -1;
-            kreg[k] = a >= 0 ? ld16(Kg + a + part * 16) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int vi = tid + k * NT;
-            const int kp = vi / DP, part = vi - (vi / DP) * DP;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int32_t j = c0 + 2 * kp + h;
-                int64_t a = (j >= key_lo && j < key_hi) ? key_addr(j) : -1;
-                vreg[k][h] = a >= 0 ? ld16(Vg + a + part * 16) : u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int k = 0; k < KPT; ++k) {
-            const int ci = tid + k * NT;
-            const int kk = ci / DP, part = ci - (ci / DP) * DP;
-            st16(sK + kk * KST + part * 16, kreg[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int vi = tid + k * NT;
-            const int kp = vi / DP, part = vi - (vi / DP) * DP;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a = word(vreg[k][0], w), b = word(vreg[k][1], w);
-                const int d = part * 8 + 2 * w;
-                *reinterpret_cast<uint32_t*>(sV + d * VST + C::vcol(d, kp) * 4) = pair_lo(a, b);
-                *reinterpret_cast<uint32_t*>(sV + (d + 1) * VST + C::vcol(d + 1, kp) * 4) = pair_hi(a, b);
-            }
+        for (int m = 0; m < IPW; ++m) {
+            const int I = wave + NW * m;
+            const int place = I * 64 + lane;
+            const int r = place / RC, cs = place - (place / RC) * RC;
+            const int32_t j = c0 + r;
+            const int64_t a = key_addr(j, chunk_ok && j >= key_lo && j < key_hi);
+            const int off = C::unswz(r, cs) * 16;
+            const uint8_t* ks = a >= 0 ? Kg + a + off : kZeroRow + off;
+            const uint8_t* vs = a >= 0 ? Vg + a + off : kZeroRow + off;
+            dma16(ks, (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024)));
+            dma16(vs, (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024)));
         }
     };
     // Stage the block ids of [blk, blk + kIdWindow) (paged): every thread calls it.
-    auto stage_ids = [&](int32_t blk) {
+    auto stage_ids = [&](int32_t blk) __attribute__((always_inline)) {
         __syncthreads();
         for (int k = tid; k < kIdWindow; k += NT) {
             const int32_t b = blk + k;
@@ -222,7 +272,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
         id_base = blk;
         __syncthreads();
     };
-    auto ensure_ids = [&](int32_t c) {
+    auto ensure_ids = [&](int32_t c) __attribute__((always_inline)) {
         if constexpr (PAGED) {
             const int32_t b_lo = (c_base + c * BN) >> 4;
             const int32_t b_hi = (c_base + c * BN + BN - 1) >> 4;
@@ -230,97 +280,139 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
         }
     };
 
-    if (c_first < c_end) {
-        ensure_ids(c_first);
-        fetch(c_first);
-    }
-    for (int32_t c = c_first; c < c_end; ++c) {
-        __syncthreads();                          // previous chunk's LDS reads are done
-        stage();
-        __syncthreads();
-        if (c + 1 < c_end) {
-            ensure_ids(c + 1);
-            fetch(c + 1);                         // in flight during this chunk's math
-        }
+    auto compute = [&](int32_t c, const uint8_t* sKb, const uint8_t* sVb) __attribute__((always_inline)) {
         const int32_t c0 = c_base + c * BN;
-
-        // ---- S^T = K . Q^T for this wave's 16 rows and the chunk's BN keys ----
-        f32x4_t st[KT];
+        // ---- S^T = K . Q^T for this wave's RT x 16 rows and the chunk's BN keys ----
+        f32x4_t st[RT][KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-            st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) st[rt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(sK + (kt * 16 + lr) * KST + (ks * 32 + 8 * lq) * 2);
-                st[kt] = mfma16(a, qf[ks], st[kt]);
+                const int row = kt * 16 + lr;
+                const u32x4 a = *reinterpret_cast<const u32x4*>(sKb + row * RB + C::swz(row, ks * 4 + lq) * 16);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) st[rt][kt] = mfma16(a, qf[rt][ks], st[rt][kt]);
             }
         }
-        // ---- mask, online softmax (row = lr; keys kt*16 + 4*lq + e) ----
-        float cmax = -INFINITY;
+        // ---- mask, online softmax (row lr of tile rt; keys kt*16 + 4*lq + e) ----
+        uint32_t pk[RT][KT][2];                   // probabilities, bf16, 4 keys per tile
+        float alpha[RT];
+        bool moved = false;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+        for (int rt = 0; rt < RT; ++rt) {
+            float cmax = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int32_t j = c0 + kt * 16 + 4 * lq + e;
-                const bool vis = j >= my_lo && j < my_hi;
-                const float v = vis ? st[kt][e] * p.scale_log2 : -INFINITY;
-                st[kt][e] = v;
-                cmax = fmaxf(cmax, v);
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t j = c0 + kt * 16 + 4 * lq + e;
+                    const bool vis = j >= my_lo[rt] && j < my_hi[rt];
+                    const float v = vis ? st[rt][kt][e] * p.scale_log2 : -INFINITY;
+                    st[rt][kt][e] = v;
+                    cmax = fmaxf(cmax, v);
+                }
+            cmax = fmaxf(cmax, xor_lanes<16>(cmax));
+            cmax = fmaxf(cmax, xor_lanes<32>(cmax));
+            const float m_new = fmaxf(m_run[rt], cmax);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            alpha[rt] = fast_exp2(m_run[rt] - m_use);
+            moved |= alpha[rt] != 1.f;
+            m_run[rt] = m_new;
+            float psum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                float pr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pr[e] = round_bf16(fast_exp2(st[rt][kt][e] - m_use));
+                    psum += pr[e];
+                }
+                pk[rt][kt][0] = pack_bf16(pr[0], pr[1]);
+                pk[rt][kt][1] = pack_bf16(pr[2], pr[3]);
             }
-        cmax = fmaxf(cmax, xor_lanes<16>(cmax));
-        cmax = fmaxf(cmax, xor_lanes<32>(cmax));
-        const float m_new = fmaxf(m_run, cmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        float psum = 0.f;
-        uint32_t pk[KT][2];                       // probabilities, bf16, 4 keys per tile
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            float pr[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pr[e] = round_bf16(fast_exp2(st[kt][e] - m_use));
-                psum += pr[e];
-            }
-            pk[kt][0] = pack_bf16(pr[0], pr[1]);
-            pk[kt][1] = pack_bf16(pr[2], pr[3]);
+            l_run[rt] = l_run[rt] * alpha[rt] + psum;
         }
-        l_run = l_run * alpha + psum;
+        if (__ballot(moved) != 0) {               // some row's max moved
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    o[rt][dt][0] *= alpha[rt]; o[rt][dt][1] *= alpha[rt];
+                    o[rt][dt][2] *= alpha[rt]; o[rt][dt][3] *= alpha[rt];
+                }
         }
         // ---- O^T += V^T . P^T, 32 keys per step: tiles (2s, 2s+1) ----
 #pragma unroll
         for (int s2 = 0; s2 < KT / 2; ++s2) {
-            const u32x4 b = u32x4{pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]};
+            u32x4 b[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                b[rt] = u32x4{pk[rt][2 * s2][0], pk[rt][2 * s2][1], pk[rt][2 * s2 + 1][0], pk[rt][2 * s2 + 1][1]};
             const int kk0 = s2 * 32 + 4 * lq;
+            // A = V^T rows d = dt*16 + lr, keys {kk0..kk0+3, kk0+16..kk0+19}: two
+            // transposing reads of row-major V; lane (4m + c) of a 16-lane group
+            // names row kk0 + m, elements dt*16 + 4c .. +3 (8 bytes of a 16-byte column).
+            const int vr0 = kk0 + (lr >> 2), vr1 = vr0 + 16;
+            const int half = (lr & 1) * 8;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 16 + lr;
-                const uint8_t* vrow = sV + d * VST;
-                const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + C::vcol(d, kk0 / 2) * 4);
-                const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + C::vcol(d, (kk0 + 16) / 2) * 4);
-                o[dt] = mfma16(u32x4{lo4.x, lo4.y, hi4.x, hi4.y}, b, o[dt]);
+                const int cl = 2 * dt + ((lr & 3) >> 1);
+                const v4i16 lo4 = ds_read_tr16(sVb + vr0 * RB + C::swz(vr0, cl) * 16 + half);
+                const v4i16 hi4 = ds_read_tr16(sVb + vr1 * RB + C::swz(vr1, cl) * 16 + half);
+                const u32x4 a = u32x4{pair_bits(lo4, 0), pair_bits(lo4, 1), pair_bits(hi4, 0), pair_bits(hi4, 1)};
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma16(a, b[rt], o[rt][dt]);
             }
         }
+    };
+
+    // Chunk i of this work group (i = 0 .. n-1) is chunk c_first + i, staged
+    // in stage i % NS.  Step i: wait for this wave's loads of chunk i
+    // (the loads of the NS - 2 later chunks stay in flight), barrier (all
+    // waves' loads of chunk i have landed; every wave is done with chunk i-1),
+    // issue chunk i + NS - 1 into chunk i-1's stage, compute chunk i.
+    // Loads past the range read the zero row, so every step waits for the
+    // same count.
+    const int32_t n = c_end > c_first ? c_end - c_first : 0;
+    if (n > 0) {
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s) {
+            if (s < n) ensure_ids(c_first + s);
+            issue(c_first + s, s);
+        }
+        for (int32_t i = 0; i < n; ++i) {
+            wait_vm<2 * IPW * (NS - 2)>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (i + NS - 1 < n) ensure_ids(c_first + i + NS - 1);
+            issue(c_first + i + NS - 1, (i + NS - 1) % NS);
+            const int st = i % NS;
+            compute(c_first + i, &sKV[st][0], &sKV[st][CB]);
+        }
+        wait_vm<0>();                             // no load may land after the work group ends
     }
 
-    // Row sum across the 4 lane groups.
-    l_run += xor_lanes<16>(l_run);
-    l_run += xor_lanes<32>(l_run);
+    // Row sums across the 4 lane groups.
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        l_run[rt] += xor_lanes<16>(l_run[rt]);
+        l_run[rt] += xor_lanes<32>(l_run[rt]);
+    }
 
-    // This lane holds O^T[d][row] for d = dt*16 + 4*lq + e.
-    const int64_t orow = ((int64_t)(ui.q_start + my_i) * p.q_heads + (int64_t)g * G + my_h) * D;
+    // This lane holds O^T[d][row] for d = dt*16 + 4*lq + e of each of its rows.
     if (S == 1) {
-        if (in_rows) {
-            const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (!in_rows[rt]) continue;
+            const int64_t orow = ((int64_t)(ui.q_start + my_i[rt]) * p.q_heads + (int64_t)g * G + my_h[rt]) * D;
+            const float inv = l_run[rt] > 0.f ? 1.f / l_run[rt] : 0.f;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int d = dt * 16 + 4 * lq;
-                const uint2 w2 = uint2{pack_bf16(o[dt][0] * inv, o[dt][1] * inv),
-                                       pack_bf16(o[dt][2] * inv, o[dt][3] * inv)};
+                const uint2 w2 = uint2{pack_bf16(o[rt][dt][0] * inv, o[rt][dt][1] * inv),
+                                       pack_bf16(o[rt][dt][2] * inv, o[rt][dt][3] * inv)};
                 *reinterpret_cast<uint2*>((uint16_t*)p.out + orow + d) = w2;
             }
         }
@@ -329,14 +421,17 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
 
     // ---- split-K partials: [unit, kv head, tile, split][BM][D] and (m, l) ----
     const int64_t wi = (((int64_t)u * Hkv + g) * T + tile) * S + split;
-    const int rloc = wave * 16 + lr;
-    float* po = p.mws_o + (wi * BM + rloc) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        st_agent2(po + dt * 16 + 4 * lq, o[dt][0], o[dt][1]);
-        st_agent2(po + dt * 16 + 4 * lq + 2, o[dt][2], o[dt][3]);
+    for (int rt = 0; rt < RT; ++rt) {
+        const int rloc = (wave * RT + rt) * 16 + lr;
+        float* po = p.mws_o + (wi * BM + rloc) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            st_agent2(po + dt * 16 + 4 * lq, o[rt][dt][0], o[rt][dt][1]);
+            st_agent2(po + dt * 16 + 4 * lq + 2, o[rt][dt][2], o[rt][dt][3]);
+        }
+        if (lq == 0) st_agent2(&p.mws_ml[(wi * BM + rloc) * 2], m_run[rt], l_run[rt]);
     }
-    if (lq == 0) st_agent2(&p.mws_ml[(wi * BM + rloc) * 2], m_run, l_run);
     wait_vm_all();
     __syncthreads();
     int32_t* ticket = p.mws_ticket + (((int64_t)u * Hkv + g) * T + tile) * kTicketStride;
@@ -396,29 +491,37 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
     }
 }
 
-int32_t mfma_rows_per_group(int32_t head_dim) { return head_dim == 64 ? 16 * 4 : 16 * 8; }
-int32_t mfma_chunk_keys(int32_t head_dim) { return head_dim == 256 ? 32 : 64; }
+template <int D>
+constexpr int32_t shape_rows() { return 16 * MfmaShape<D>::NW * MfmaShape<D>::RT; }
+
+int32_t mfma_rows_per_group(int32_t head_dim) {
+    return head_dim == 64 ? shape_rows<64>() : head_dim == 128 ? shape_rows<128>() : shape_rows<256>();
+}
+int32_t mfma_chunk_keys(int32_t head_dim) {
+    return head_dim == 64 ? MfmaShape<64>::BN : head_dim == 128 ? MfmaShape<128>::BN : MfmaShape<256>::BN;
+}
 
 bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim) {
     return dtype == PKV_BF16 && (head_dim == 64 || head_dim == 128 || head_dim == 256);
 }
 
-template <int D, int NW, int BN>
+template <int D>
 static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
+    using Sh = MfmaShape<D>;
     dim3 grid(p.mfma_tiles * p.mfma_splits, p.kv_heads, p.num_units);
     if (p.mode == kColumn) {
-        attn_mfma_kernel<D, NW, BN, false><<<grid, dim3(64 * NW), 0, stream>>>(p);
+        attn_mfma_kernel<D, Sh::NW, Sh::RT, Sh::BN, Sh::NS, Sh::WPE, false><<<grid, dim3(64 * Sh::NW), 0, stream>>>(p);
     } else {
-        attn_mfma_kernel<D, NW, BN, true><<<grid, dim3(64 * NW), 0, stream>>>(p);
+        attn_mfma_kernel<D, Sh::NW, Sh::RT, Sh::BN, Sh::NS, Sh::WPE, true><<<grid, dim3(64 * Sh::NW), 0, stream>>>(p);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_attn_mfma(const AttnParams& p, pkv_dtype dtype, int32_t head_dim, hipStream_t stream) {
     if (!attn_mfma_supported(dtype, head_dim)) return hipErrorInvalidValue;
-    if (head_dim == 64) return launch_mfma_t<64, 4, 64>(p, stream);
-    if (head_dim == 128) return launch_mfma_t<128, 8, 64>(p, stream);
-    return launch_mfma_t<256, 8, 32>(p, stream);
+    if (head_dim == 64) return launch_mfma_t<64>(p, stream);
+    if (head_dim == 128) return launch_mfma_t<128>(p, stream);
+    return launch_mfma_t<256>(p, stream);
 }
 
 }  // namespace pkv

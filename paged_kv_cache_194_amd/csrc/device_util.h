@@ -129,6 +129,16 @@ __device__ __forceinline__ void st_agent2(float* p, float a, float b) {
                        ((uint64_t)__builtin_bit_cast(uint32_t, b) << 32);
     __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Work-group barrier that orders LDS only: this wave's LDS accesses have
+// completed when it passes, while its global loads stay in flight (a full
+// __syncthreads() would also wait for those).
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Wait until every vector memory access this wave issued has completed.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
