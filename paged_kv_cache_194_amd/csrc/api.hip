@@ -86,7 +86,8 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
     pl.gt = pkv::vec_group_rows(group);
     if (pl.vec && pl.splits > 1) {
         pl.vec_ticket = pkv::ticket_bytes(U, kv_heads);
-        pl.vec_bytes = (size_t)U * kv_heads * pl.splits * pl.gt * ((size_t)head_dim + 2) * sizeof(float);
+        pl.vec_bytes = (size_t)pkv::vec_slots(U, pl.splits) * kv_heads * pl.gt * ((size_t)head_dim + 2) *
+                       sizeof(float);
     }
     if (pl.mfma) {
         pl.bm = pkv::mfma_rows_per_group(head_dim);
@@ -116,8 +117,9 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
     p.num_splits = pl.splits;
     p.ws_ticket = nullptr;
     p.ws_o = p.ws_ml = nullptr;
+    p.vec_wgs = pkv::vec_slots(p.num_units, pl.splits);
     if (pl.vec_bytes) {
-        const size_t n = (size_t)p.num_units * p.kv_heads * pl.splits * pl.gt;
+        const size_t n = (size_t)p.vec_wgs * p.kv_heads * pl.gt;
         p.ws_ticket = (int32_t*)ws;
         p.ws_o = (float*)(ws + pl.vec_ticket);
         p.ws_ml = p.ws_o + n * head_dim;

@@ -77,6 +77,22 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     }
 }
 
+// Live 16-key blocks of unit u for the vector path, or -1 when the unit is
+// not this path's (several query rows, or its row outside the output).
+__device__ __forceinline__ int32_t vec_unit_blocks(const AttnParams& p, int32_t u) {
+    const UnitInfo ui = load_unit(p, u);
+    if (ui.q_len != 1 || ui.q_start < 0 || ui.q_start >= p.total_q) return -1;
+    const int32_t E = ui.keys_ok ? ui.kv_end : 0;
+    const int32_t lo = (p.window > 0 && E - p.window > 0) ? E - p.window : 0;
+    const int32_t b_end = (E + 15) >> 4, b_first = lo >> 4;
+    return b_end > b_first ? b_end - b_first : 0;
+}
+
+// Work groups a unit of nb live blocks gets at bps blocks per work group.
+__device__ __forceinline__ int32_t vec_unit_wgs(int32_t nb, int32_t bps) {
+    return nb < 0 ? 0 : (nb <= bps ? 1 : (nb + bps - 1) / bps);
+}
+
 // Log-sum-exp merge of this lane's (M, tot, o) with lane (lane ^ ST)'s.
 template <int ST>
 __device__ __forceinline__ void combine_lanes(float& M, float& tot, float4& o) {
@@ -101,19 +117,20 @@ __device__ __forceinline__ void combine_lanes(float& M, float& tot, float4& o) {
 // Splits past S are clamped to S-1 and weighted 0; an empty split (m = -inf)
 // gets weight 0.  The NP lane results meet through lane swizzles.
 template <typename T, int D, int GT>
-__device__ __forceinline__ void merge_splits(const AttnParams& p, int32_t u, int32_t g, int32_t row) {
+__device__ __forceinline__ void merge_splits(const AttnParams& p, int32_t g, int32_t row, int32_t slot0,
+                                             int32_t S) {
     constexpr int ITEMS = GT * (D / 4);
     constexpr int NP = ITEMS >= kThreads ? 1 : (kThreads / ITEMS > 16 ? 16 : kThreads / ITEMS);
     constexpr int CH = NP == 1 ? 32 : NP == 2 ? 16 : 8;
-    const int32_t S = p.num_splits, G = p.group, Hkv = p.kv_heads;
-    const int64_t w0 = ((int64_t)u * Hkv + g) * S;
+    const int32_t G = p.group, Hkv = p.kv_heads;
+    const int64_t w0 = (int64_t)slot0 * Hkv + g;
     const int part = threadIdx.x % NP;
     for (int item = threadIdx.x / NP; item < ITEMS; item += kThreads / NP) {
         const int r = item / (D / 4), d4 = (item - r * (D / 4)) * 4;
         if (r >= G) continue;                   // uniform over the NP lanes of an item
         const float* osrc = p.ws_o + (w0 * GT + r) * D + d4;
         const float* msrc = p.ws_ml + (w0 * GT + r) * 2;
-        const int64_t ostride = (int64_t)GT * D, mstride = (int64_t)GT * 2;
+        const int64_t ostride = (int64_t)Hkv * GT * D, mstride = (int64_t)Hkv * GT * 2;
         float M = -INFINITY, tot = 0.f;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s0 = 0; s0 < S; s0 += NP * CH) {
@@ -168,15 +185,64 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     __shared__ float sLv[kWaves][C::VR][GT];
     __shared__ float sM[kWaves][GT];
     __shared__ int sLast;
+    __shared__ int32_t sWork[5];
 
-    const int32_t split = blockIdx.x;
     const int32_t g = blockIdx.y;
-    const int32_t u = blockIdx.z;
     const int lane = lane_id();
     const int wave = threadIdx.x >> 6;
     const int kpart = lane % KLPT, ktok = lane / KLPT;
     const int vpart = lane % VLPT, vtok = lane / VLPT;
-    const int32_t S = p.num_splits;
+
+    // Which unit and split this work group takes (slot = blockIdx.x):
+    //  - one unit: split = slot of num_splits;
+    //  - one split per unit: unit = slot;
+    //  - otherwise the units' live blocks are dealt evenly over the
+    //    num_splits * units work groups: bps = ceil(total blocks / work groups),
+    //    and a unit of nb blocks gets ceil(nb / bps) consecutive slots (at
+    //    least one, so that an empty unit still writes its zero row).
+    int32_t u, split, S, slot0, bps = -1;
+    if (p.num_units == 1) {
+        u = 0; split = blockIdx.x; S = p.num_splits; slot0 = 0;
+    } else if (p.num_splits == 1) {
+        u = blockIdx.x; split = 0; S = 1; slot0 = u;
+    } else {
+        if (wave == 0) {
+            const int32_t U = p.num_units;
+            const int64_t W = (int64_t)p.num_splits * U;
+            const int32_t per = (U + 63) / 64;
+            const int32_t ub = lane * per, ue = min(U, ub + per);
+            int64_t tb = 0;
+            for (int32_t uu = ub; uu < ue; ++uu) {
+                const int32_t nb = vec_unit_blocks(p, uu);
+                tb += nb > 0 ? nb : 0;
+            }
+#pragma unroll
+            for (int st = 1; st < 64; st *= 2) tb += __shfl_xor(tb, st, 64);
+            const int32_t b = (int32_t)((tb + W - 1) / W);
+            const int32_t bp = b > 1 ? b : 1;
+            int32_t cnt = 0;
+            for (int32_t uu = ub; uu < ue; ++uu) cnt += vec_unit_wgs(vec_unit_blocks(p, uu), bp);
+            int32_t incl = cnt;
+#pragma unroll
+            for (int st = 1; st < 64; st *= 2) {
+                const int32_t y = __shfl_up(incl, st, 64);
+                if (lane >= st) incl += y;
+            }
+            if (lane == 0) sWork[0] = -1;
+            int32_t acc = incl - cnt;
+            const int32_t w = blockIdx.x;
+            for (int32_t uu = ub; uu < ue; ++uu) {
+                const int32_t n = vec_unit_wgs(vec_unit_blocks(p, uu), bp);
+                if (w >= acc && w < acc + n) {
+                    sWork[0] = uu; sWork[1] = w - acc; sWork[2] = n; sWork[3] = acc; sWork[4] = bp;
+                }
+                acc += n;
+            }
+        }
+        __syncthreads();
+        u = sWork[0]; split = sWork[1]; S = sWork[2]; slot0 = sWork[3]; bps = sWork[4];
+        if (u < 0) return;                          // a spare slot
+    }
 
     const UnitInfo ui = load_unit(p, u);
     if (ui.q_len != 1) return;                      // other units are not this path's
@@ -192,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     const int32_t b_end = (hi + 15) >> 4;
     const int32_t b_first = lo >> 4;
     const int32_t nblk = b_end > b_first ? b_end - b_first : 0;
-    const int32_t bps = (nblk + S - 1) / S;
+    if (bps < 0) bps = (nblk + S - 1) / S;
     const int32_t sb = b_first + split * bps;
     const int32_t se = min(b_end, sb + bps);
     int32_t ids = -1;               // lane i: pool block of this wave's i-th block
@@ -481,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     }
     __syncthreads();
 
-    const int64_t wi = ((int64_t)u * Hkv + g) * S + split;
+    const int64_t wi = (int64_t)(slot0 + split) * Hkv + g;
     for (int idx = threadIdx.x; idx < GT * (D / 2); idx += kThreads) {
         const int r = idx / (D / 2), d = (idx - r * (D / 2)) * 2;
         if (r >= G) continue;
@@ -533,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (threadIdx.x == 0)                       // ready for the next call
         __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_splits<T, D, GT>(p, u, g, row);
+    merge_splits<T, D, GT>(p, g, row, slot0, S);
 }
 
 // Zero the output rows that no unit covers.
@@ -564,6 +630,12 @@ int32_t vec_group_rows(int32_t group) {
     return group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
 }
 
+int32_t vec_slots(int32_t units, int32_t splits) {
+    if (units <= 1) return splits;
+    if (splits <= 1) return units;
+    return splits * units + units;
+}
+
 size_t ticket_bytes(int32_t units, int32_t kv_heads) {
     const size_t n = (size_t)units * kv_heads * kTicketStride * sizeof(int32_t);
     return (n + 255) / 256 * 256;
@@ -576,7 +648,7 @@ bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group) {
 
 template <typename T, int D, int GT>
 static hipError_t launch_vec_t(const AttnParams& p, hipStream_t stream) {
-    dim3 grid(p.num_splits, p.kv_heads, p.num_units);
+    dim3 grid(p.vec_wgs, p.kv_heads, 1);
     if (p.mode == kColumn) {
         attn_vec_kernel<T, D, GT, false><<<grid, dim3(kThreads), 0, stream>>>(p);
     } else {

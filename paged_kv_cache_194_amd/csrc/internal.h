@@ -27,8 +27,8 @@ struct AttnParams {
     const int32_t* seq_info;
     const void* k_new;     // fused append (paged decode): [units, Hkv, D] or null
     const void* v_new;
-    float* ws_o;           // split-K partial outputs [units*Hkv*splits][GT][D]
-    float* ws_ml;          // split-K partial (max, sum) [units*Hkv*splits][GT][2]
+    float* ws_o;           // split-K partial outputs [vec_wgs][Hkv][GT][D]
+    float* ws_ml;          // split-K partial (max, sum) [vec_wgs][Hkv][GT][2]
     int32_t* ws_ticket;    // per (unit, kv head) arrival counters, zero between calls
     float* mws_o;          // matrix-core path partials [units*Hkv*tiles*splits][BM][D]
     float* mws_ml;         // and their (max, sum) [..][BM][2]
@@ -49,7 +49,8 @@ struct AttnParams {
     int32_t group;         // q_heads / kv_heads
     int32_t causal;
     int32_t window;
-    int32_t num_splits;
+    int32_t num_splits;    // vector path: split-K partitions per unit (on average)
+    int32_t vec_wgs;       // vector path: work-group slots per kv head
     float scale_log2;      // softmax_scale * log2(e)
 };
 
@@ -119,5 +120,10 @@ constexpr int32_t kTicketStride = 64;
 
 // Bytes of the arrival counters at the start of a split-K workspace.
 size_t ticket_bytes(int32_t units, int32_t kv_heads);
+
+// Work-group slots per kv head of the vector path for `units` units at
+// `splits` partitions per unit: the balanced deal over several units can
+// round up once per unit.
+int32_t vec_slots(int32_t units, int32_t splits);
 
 }  // namespace pkv
