@@ -187,13 +187,16 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     __shared__ int sLast;
     __shared__ int32_t sWork[5];
 
-    const int32_t g = blockIdx.y;
+    // The kv head is the fastest grid dimension: the work groups reading the
+    // heads of the same blocks run together and share DRAM rows.
+    const int32_t g = blockIdx.x;
+    const int32_t slot = blockIdx.y;
     const int lane = lane_id();
     const int wave = threadIdx.x >> 6;
     const int kpart = lane % KLPT, ktok = lane / KLPT;
     const int vpart = lane % VLPT, vtok = lane / VLPT;
 
-    // Which unit and split this work group takes (slot = blockIdx.x):
+    // Which unit and split this work group takes (slot = blockIdx.y):
     //  - one unit: split = slot of num_splits;
     //  - one split per unit: unit = slot;
     //  - otherwise the units' live blocks are dealt evenly over the
@@ -202,9 +205,9 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     //    least one, so that an empty unit still writes its zero row).
     int32_t u, split, S, slot0, bps = -1;
     if (p.num_units == 1) {
-        u = 0; split = blockIdx.x; S = p.num_splits; slot0 = 0;
+        u = 0; split = slot; S = p.num_splits; slot0 = 0;
     } else if (p.num_splits == 1) {
-        u = blockIdx.x; split = 0; S = 1; slot0 = u;
+        u = slot; split = 0; S = 1; slot0 = u;
     } else {
         if (wave == 0) {
             const int32_t U = p.num_units;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             }
             if (lane == 0) sWork[0] = -1;
             int32_t acc = incl - cnt;
-            const int32_t w = blockIdx.x;
+            const int32_t w = slot;
             for (int32_t uu = ub; uu < ue; ++uu) {
                 const int32_t n = vec_unit_wgs(vec_unit_blocks(p, uu), bp);
                 if (w >= acc && w < acc + n) {
@@ -648,7 +651,7 @@ bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group) {
 
 template <typename T, int D, int GT>
 static hipError_t launch_vec_t(const AttnParams& p, hipStream_t stream) {
-    dim3 grid(p.vec_wgs, p.kv_heads, 1);
+    dim3 grid(p.kv_heads, p.vec_wgs, 1);
     if (p.mode == kColumn) {
         attn_vec_kernel<T, D, GT, false><<<grid, dim3(kThreads), 0, stream>>>(p);
     } else {
