@@ -141,9 +141,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 
     const int32_t T = p.mfma_tiles;               // row tiles per (unit, kv head)
     const int32_t S = p.mfma_splits;
-    const int32_t tile = blockIdx.x / S;
-    const int32_t split = blockIdx.x - tile * S;
-    const int32_t g = blockIdx.y;
+    // kv head fastest: the work groups reading the heads of the same keys run together.
+    const int32_t g = blockIdx.x;
+    const int32_t tile = blockIdx.y / S;
+    const int32_t split = blockIdx.y - tile * S;
     const int32_t u = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -508,7 +509,7 @@ bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim) {
 template <int D>
 static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
     using Sh = MfmaShape<D>;
-    dim3 grid(p.mfma_tiles * p.mfma_splits, p.kv_heads, p.num_units);
+    dim3 grid(p.kv_heads, p.mfma_tiles * p.mfma_splits, p.num_units);
     if (p.mode == kColumn) {
         attn_mfma_kernel<D, Sh::NW, Sh::RT, Sh::BN, Sh::NS, Sh::WPE, false><<<grid, dim3(64 * Sh::NW), 0, stream>>>(p);
     } else {
