@@ -605,15 +605,19 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     merge_splits<T, D, GT>(p, g, row, slot0, S);
 }
 
-// Zero the output rows that no unit covers.
+// Zero the output rows that no unit covers: one lane per row.  The unit index
+// of the scan is the same in every lane, so the unit table is read with
+// broadcast (scalar) loads; each wave then clears its uncovered rows together,
+// 16 bytes per lane.
 __global__ __launch_bounds__(256) void zero_uncovered_kernel(AttnParams p, int32_t row_bytes) {
-    const int32_t r = blockIdx.x;
-    bool covered = false;
-    for (int32_t u = 0; u < p.num_units && !covered; ++u) {
+    const int lane = lane_id();
+    const int32_t r = blockIdx.x * 256 + threadIdx.x;
+    bool covered = r >= p.total_q;                  // past the end: nothing to write
+    for (int32_t u = 0; u < p.num_units; ++u) {
         int32_t q0, L;
         if (p.mode == kColumn) {
-            q0 = p.seq_info[4 * u];
-            L = p.seq_info[4 * u + 1];
+            q0 = p.seq_info[4 * (int64_t)u];
+            L = p.seq_info[4 * (int64_t)u + 1];
         } else if (p.mode == kPagedVarlen) {
             q0 = p.cu_seqlens_q[u];
             L = p.cu_seqlens_q[u + 1] - q0;
@@ -622,11 +626,16 @@ __global__ __launch_bounds__(256) void zero_uncovered_kernel(AttnParams p, int32
             L = 1;
         }
         if (L > p.max_seqlen_q) L = p.max_seqlen_q;
-        covered = (r >= q0) && (L > 0) && (r - q0 < L);
+        covered |= (r >= q0) && (r - q0 < L);
     }
-    if (covered) return;
-    uint8_t* o = (uint8_t*)p.out + (int64_t)r * row_bytes;
-    for (int32_t c = threadIdx.x; c < row_bytes / 16; c += blockDim.x) st16(o + (int64_t)c * 16, u32x4{0u, 0u, 0u, 0u});
+    uint64_t todo = __ballot(!covered);
+    const int32_t r0 = r - lane;                    // first row of this wave
+    while (todo != 0) {
+        const int i = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        uint8_t* o = (uint8_t*)p.out + (int64_t)(r0 + i) * row_bytes;
+        for (int32_t c = lane; c < row_bytes / 16; c += 64) st16(o + (int64_t)c * 16, u32x4{0u, 0u, 0u, 0u});
+    }
 }
 
 int32_t vec_group_rows(int32_t group) {
@@ -709,7 +718,7 @@ hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t h
                                  hipStream_t stream) {
     const int32_t row_bytes = p.q_heads * head_dim * (dtype == PKV_BF16 ? 2 : 4);
     if (p.total_q <= 0) return hipSuccess;
-    zero_uncovered_kernel<<<dim3(p.total_q), dim3(256), 0, stream>>>(p, row_bytes);
+    zero_uncovered_kernel<<<dim3((p.total_q + 255) / 256), dim3(256), 0, stream>>>(p, row_bytes);
     return hipGetLastError();
 }
 
