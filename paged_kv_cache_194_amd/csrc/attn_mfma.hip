@@ -188,12 +188,17 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 
     // This lane's rows: row lr of the wave's tiles rt = 0 .. RT-1.
     int32_t my_i[RT], my_h[RT], my_lo[RT], my_hi[RT];
-    bool in_rows[RT];
+    bool in_rows[RT], rows_ok[RT];
     u32x4 qf[RT][KS];                             // Q^T operand: d = ks*32 + 8*lq .. +7
+    // Scores are scaled inside the exponent's fma by |scale|; a negative scale
+    // flips the sign of q instead (exact in bf16).
+    const float sc = fabsf(p.scale_log2);
+    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int32_t mm = m0 + (wave * RT + rt) * 16 + lr;
         const bool row_ok = mm < M;
+        rows_ok[rt] = row_ok;
         my_i[rt] = row_ok ? mm / G : 0;
         my_h[rt] = row_ok ? mm - my_i[rt] * G : 0;
         my_lo[rt] = lo_of(my_i[rt]);
@@ -203,7 +208,12 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
                             (((int64_t)(ui.q_start + my_i[rt]) * p.q_heads + (int64_t)g * G + my_h[rt]) * D) * 2;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qf[rt][ks] = in_rows[rt] ? ld16(qb + (ks * 32 + 8 * lq) * 2) : u32x4{0u, 0u, 0u, 0u};
+            if (in_rows[rt]) {
+                const u32x4 x = ld16(qb + (ks * 32 + 8 * lq) * 2);
+                qf[rt][ks] = u32x4{x.x ^ qsign, x.y ^ qsign, x.z ^ qsign, x.w ^ qsign};
+            } else {
+                qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
+            }
     }
     // Q complete before the pipeline starts: otherwise the first use of qf in the
     // chunk loop would wait for every load in flight.
@@ -297,26 +307,43 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
                 for (int rt = 0; rt < RT; ++rt) st[rt][kt] = mfma16(a, qf[rt][ks], st[rt][kt]);
             }
         }
-        // ---- mask, online softmax (row lr of tile rt; keys kt*16 + 4*lq + e) ----
+        // ---- online softmax (row lr of tile rt; keys kt*16 + 4*lq + e) ----
+        // A chunk inside every row's visible range (the common case) needs no
+        // per-key mask: a wave-uniform test picks that path.  Rows past M are
+        // never written, so they do not force the mask.
+        bool edge = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            edge |= rows_ok[rt] && !(my_lo[rt] <= c0 && c0 + BN <= my_hi[rt]);
+        const bool masked = __ballot(edge) != 0;
         uint32_t pk[RT][KT][2];                   // probabilities, bf16, 4 keys per tile
         float alpha[RT];
         bool moved = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
+            uint32_t vis = ~0u;                   // bit kt*4 + e: key visible to this row
             float cmax = -INFINITY;
+            if (masked) {
+                vis = 0u;
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+                for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int32_t j = c0 + kt * 16 + 4 * lq + e;
-                    const bool vis = j >= my_lo[rt] && j < my_hi[rt];
-                    const float v = vis ? st[rt][kt][e] * p.scale_log2 : -INFINITY;
-                    st[rt][kt][e] = v;
-                    cmax = fmaxf(cmax, v);
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        const int32_t j = c0 + kt * 16 + 4 * lq + e;
+                        const bool v = j >= my_lo[rt] && j < my_hi[rt];
+                        vis |= (v ? 1u : 0u) << (kt * 4 + e);
+                        cmax = v ? fmaxf(cmax, st[rt][kt][e]) : cmax;
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cmax = fmaxf(cmax, st[rt][kt][e]);
+            }
             cmax = fmaxf(cmax, xor_lanes<16>(cmax));
             cmax = fmaxf(cmax, xor_lanes<32>(cmax));
-            const float m_new = fmaxf(m_run[rt], cmax);
+            const float cm = cmax == -INFINITY ? -INFINITY : cmax * sc;   // scaled, log2 units
+            const float m_new = fmaxf(m_run[rt], cm);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
             alpha[rt] = fast_exp2(m_run[rt] - m_use);
             moved |= alpha[rt] != 1.f;
@@ -327,11 +354,14 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
                 float pr[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    pr[e] = round_bf16(fast_exp2(st[rt][kt][e] - m_use));
-                    psum += pr[e];
+                    const float x = fmaf(st[rt][kt][e], sc, -m_use);
+                    pr[e] = fast_exp2(((vis >> (kt * 4 + e)) & 1u) ? x : -INFINITY);
                 }
+                // rounded to bf16 for the MFMA; the row sum adds the same rounded values
                 pk[rt][kt][0] = pack_bf16(pr[0], pr[1]);
                 pk[rt][kt][1] = pack_bf16(pr[2], pr[3]);
+                psum = dot2_bf16(pk[rt][kt][0], kBf16OnePair, psum);
+                psum = dot2_bf16(pk[rt][kt][1], kBf16OnePair, psum);
             }
             l_run[rt] = l_run[rt] * alpha[rt] + psum;
         }

@@ -35,10 +35,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
 }
 
-// Two fp32 values rounded to bf16 and packed (a in the low half).
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (nearest even) and packed, a in the low
+// half: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    const f32x2v_t x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v_t));
 }
+
+// Packed bf16 pair (1.0, 1.0): dot2 with it sums the pair in fp32.
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 
 // Round an fp32 value to the nearest bf16 value, kept in fp32.
 __device__ __forceinline__ float round_bf16(float f) {
