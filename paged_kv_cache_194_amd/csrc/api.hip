@@ -55,6 +55,15 @@ int32_t clamp_splits(int64_t s, int64_t cap) {
     return (int32_t)(s < 1 ? 1 : s);
 }
 
+// Compute units of the current device (256 on MI355X if the query fails).
+int32_t device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
 // Vector path: about 2048 work groups, at least 8 blocks (two per wave) each.
 int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_splits) {
     if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
@@ -96,8 +105,12 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
         const int64_t base = (int64_t)U * kv_heads * pl.tiles;
         const int64_t chunks = ((int64_t)(keys > 0 ? keys : 1) + pkv::mfma_chunk_keys(head_dim) - 1) /
                                pkv::mfma_chunk_keys(head_dim);
+        // Library choice: about one round of work groups on the device (the
+        // dealt splits are equal in size, and every split adds a BM x D partial
+        // to merge), at least 8 chunks per split.
+        const int64_t round = (int64_t)device_cus() * pkv::mfma_groups_per_cu(head_dim);
         pl.msplits = num_splits > 0 ? clamp_splits(num_splits, chunks)
-                                    : clamp_splits((512 + base - 1) / base, chunks / 2 > 0 ? chunks / 2 : 1);
+                                    : clamp_splits((round + base / 2) / base, chunks / 8 > 0 ? chunks / 8 : 1);
         if (pl.msplits > 1) {
             pl.mfma_ticket = pkv::ticket_bytes(U * pl.tiles, kv_heads);
             pl.mfma_bytes = (size_t)base * pl.msplits * pl.bm * ((size_t)head_dim + 2) * sizeof(float);

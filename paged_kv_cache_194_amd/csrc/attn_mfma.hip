@@ -128,6 +128,46 @@ struct MfmaCfg {
     }
 };
 
+// Keys one row tile of a unit needs: the union of its rows' visible ranges,
+// from a 16-aligned start, in chunks of `bn` keys.  Row i of a unit of L rows
+// over E keys sits at position E - L + i (causal: keys up to it; window W:
+// the W keys ending there).
+struct TileKeys {
+    int32_t key_lo, key_hi, c_base, nchunk;
+};
+__device__ __forceinline__ int32_t row_lo(const AttnParams& p, int32_t E, int32_t L, int32_t i) {
+    if (p.window <= 0) return 0;
+    const int32_t lo = E - L + i - p.window + 1;
+    return lo > 0 ? lo : 0;
+}
+__device__ __forceinline__ int32_t row_hi(const AttnParams& p, int32_t E, int32_t L, int32_t i) {
+    if (!p.causal) return E;
+    const int32_t pos1 = E - L + i + 1;
+    return pos1 < E ? (pos1 > 0 ? pos1 : 0) : E;
+}
+__device__ __forceinline__ TileKeys tile_keys(const AttnParams& p, int32_t E, int32_t L, int32_t M,
+                                              int32_t m0, int32_t bm, int32_t bn) {
+    const int32_t G = p.group;
+    const int32_t m_last = min(M, m0 + bm) - 1;
+    TileKeys t;
+    t.key_lo = row_lo(p, E, L, m0 / G);
+    t.key_hi = max(row_hi(p, E, L, m_last / G), t.key_lo);
+    t.c_base = (t.key_lo >> 4) << 4;
+    t.nchunk = t.key_hi > t.c_base ? (t.key_hi - t.c_base + bn - 1) / bn : 0;
+    return t;
+}
+// Chunks of row tile `tile` of unit u on the matrix-core path, or -1 when that
+// (unit, tile) is not this path's work.
+__device__ __forceinline__ int32_t mfma_item_chunks(const AttnParams& p, int32_t u, int32_t tile,
+                                                    int32_t bm, int32_t bn) {
+    const UnitInfo ui = load_unit(p, u);
+    const int32_t L = ui.q_len;
+    if (L <= 0 || (L == 1 && p.group <= 8)) return -1;
+    const int32_t M = (L < p.max_seqlen_q ? L : p.max_seqlen_q) * p.group;
+    if (tile * bm >= M) return -1;
+    return tile_keys(p, ui.keys_ok ? ui.kv_end : 0, L, M, tile * bm, bm, bn).nchunk;
+}
+
 template <int D, int NW, int RT, int BN, int NS, int WPE, bool PAGED>
 __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     using C = MfmaCfg<D, NW, RT, BN, NS>;
@@ -139,18 +179,75 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     __shared__ int32_t sIds[kIdWindow];
     __shared__ int32_t sLast;
 
+    __shared__ int32_t sWork[5];
     const int32_t T = p.mfma_tiles;               // row tiles per (unit, kv head)
-    const int32_t S = p.mfma_splits;
     // kv head fastest: the work groups reading the heads of the same keys run together.
     const int32_t g = blockIdx.x;
-    const int32_t tile = blockIdx.y / S;
-    const int32_t split = blockIdx.y - tile * S;
-    const int32_t u = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
     const int lr = lane & 15;                     // this lane's query row within the wave
     const int lq = lane >> 4;                     // lane group 0..3
+
+    // Work items are (unit, row tile).  With one split, or one item, slot
+    // blockIdx.y of unit blockIdx.z is (tile, split).  Otherwise the
+    // mfma_splits * items slots of a kv head are dealt over the items in
+    // proportion to their chunks: an item of n chunks gets max(1, floor(n * W'
+    // / total)) consecutive slots, W' = slots - items that have work, so the
+    // deal never needs more than the grid holds.
+    int32_t u, tile, split, S, slot0;
+    if (p.mfma_splits == 1 || p.num_units * T == 1) {
+        S = p.mfma_splits;
+        tile = blockIdx.y / S;
+        split = blockIdx.y - tile * S;
+        u = blockIdx.z;
+        slot0 = (u * T + tile) * S;
+    } else {
+        if (wave == 0) {
+            const int32_t NI = p.num_units * T;
+            const int32_t per = (NI + 63) / 64;
+            const int32_t ib = lane * per, ie = min(NI, ib + per);
+            int64_t tot = 0;
+            int32_t valid = 0;
+            for (int32_t it = ib; it < ie; ++it) {
+                const int32_t n = mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN);
+                tot += n > 0 ? n : 0;
+                valid += n >= 0 ? 1 : 0;
+            }
+#pragma unroll
+            for (int st = 1; st < 64; st *= 2) {
+                tot += __shfl_xor(tot, st, 64);
+                valid += __shfl_xor(valid, st, 64);
+            }
+            const int64_t Wp = (int64_t)p.mfma_splits * NI - valid;
+            auto slots_of = [&](int32_t n) -> int32_t {
+                if (n < 0) return 0;
+                const int64_t k = tot > 0 ? (int64_t)n * Wp / tot : 0;
+                return k > 1 ? (int32_t)k : 1;
+            };
+            int32_t cnt = 0;
+            for (int32_t it = ib; it < ie; ++it) cnt += slots_of(mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN));
+            int32_t incl = cnt;
+#pragma unroll
+            for (int st = 1; st < 64; st *= 2) {
+                const int32_t y = __shfl_up(incl, st, 64);
+                if (lane >= st) incl += y;
+            }
+            if (lane == 0) sWork[0] = -1;
+            int32_t acc = incl - cnt;
+            const int32_t w = blockIdx.y;
+            for (int32_t it = ib; it < ie; ++it) {
+                const int32_t k = slots_of(mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN));
+                if (w >= acc && w < acc + k) {
+                    sWork[0] = it / T; sWork[1] = it - (it / T) * T; sWork[2] = w - acc; sWork[3] = k; sWork[4] = acc;
+                }
+                acc += k;
+            }
+        }
+        __syncthreads();
+        u = sWork[0]; tile = sWork[1]; split = sWork[2]; S = sWork[3]; slot0 = sWork[4];
+        if (u < 0) return;                          // a spare slot
+    }
 
     const UnitInfo ui = load_unit(p, u);
     const int32_t G = p.group;
@@ -164,24 +261,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
     const int32_t Hkv = p.kv_heads;
 
-    // Visible range of position i (row i of the unit).
-    auto lo_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t {
-        if (p.window <= 0) return 0;
-        const int32_t pos = E - L + i;
-        const int32_t lo = pos - p.window + 1;
-        return lo > 0 ? lo : 0;
-    };
-    auto hi_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t {
-        if (!p.causal) return E;
-        const int32_t pos1 = E - L + i + 1;
-        return pos1 < E ? (pos1 > 0 ? pos1 : 0) : E;
-    };
-    const int32_t m_last = min(M, m0 + BM) - 1;
-    const int32_t i_first = m0 / G, i_last = m_last / G;
-    const int32_t key_lo = lo_of(i_first);                  // the union over this tile's rows
-    const int32_t key_hi = max(hi_of(i_last), key_lo);
-    const int32_t c_base = (key_lo >> 4) << 4;
-    const int32_t nchunk = key_hi > c_base ? (key_hi - c_base + BN - 1) / BN : 0;
+    // The union of this tile's rows' visible ranges, cut into S parts.
+    const TileKeys tk = tile_keys(p, E, L, M, m0, BM, BN);
+    const int32_t key_lo = tk.key_lo, key_hi = tk.key_hi, c_base = tk.c_base, nchunk = tk.nchunk;
+    auto lo_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t { return row_lo(p, E, L, i); };
+    auto hi_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t { return row_hi(p, E, L, i); };
     const int32_t cps = (nchunk + S - 1) / S;
     const int32_t c_first = split * cps;
     const int32_t c_end = min(nchunk, c_first + cps);
@@ -450,8 +534,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
         return;
     }
 
-    // ---- split-K partials: [unit, kv head, tile, split][BM][D] and (m, l) ----
-    const int64_t wi = (((int64_t)u * Hkv + g) * T + tile) * S + split;
+    // ---- split-K partials: [slot][kv head][BM][D] and (m, l) ----
+    const int64_t wi = (int64_t)(slot0 + split) * Hkv + g;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int rloc = (wave * RT + rt) * 16 + lr;
@@ -474,7 +558,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // Merge: each thread takes 4 consecutive outputs of one row, 16 splits in flight.
-    const int64_t w0 = (((int64_t)u * Hkv + g) * T + tile) * S;
+    const int64_t w0 = (int64_t)slot0 * Hkv + g;
     constexpr int CH = 16;
     for (int idx = tid; idx < BM * (D / 4); idx += NT) {
         const int r = idx / (D / 4), d4 = (idx - r * (D / 4)) * 4;
@@ -484,7 +568,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
         if (ui.q_start + ii < 0 || ui.q_start + ii >= p.total_q) continue;
         const float* osrc = p.mws_o + (w0 * BM + r) * D + d4;
         const float* msrc = p.mws_ml + (w0 * BM + r) * 2;
-        const int64_t ostride = (int64_t)BM * D, mstride = (int64_t)BM * 2;
+        const int64_t ostride = (int64_t)Hkv * BM * D, mstride = (int64_t)Hkv * BM * 2;
         float Mx = -INFINITY, tot = 0.f;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s0 = 0; s0 < S; s0 += CH) {
@@ -528,6 +612,11 @@ constexpr int32_t shape_rows() { return 16 * MfmaShape<D>::NW * MfmaShape<D>::RT
 int32_t mfma_rows_per_group(int32_t head_dim) {
     return head_dim == 64 ? shape_rows<64>() : head_dim == 128 ? shape_rows<128>() : shape_rows<256>();
 }
+// Work groups of the matrix-core kernel one CU holds at once (LDS and
+// register budgets of the shape: 68 KiB / 2 waves per SIMD at D <= 128,
+// 132 KiB at D = 256).
+int32_t mfma_groups_per_cu(int32_t head_dim) { return head_dim == 256 ? 1 : 2; }
+
 int32_t mfma_chunk_keys(int32_t head_dim) {
     return head_dim == 64 ? MfmaShape<64>::BN : head_dim == 128 ? MfmaShape<128>::BN : MfmaShape<256>::BN;
 }
@@ -539,7 +628,8 @@ bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim) {
 template <int D>
 static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
     using Sh = MfmaShape<D>;
-    dim3 grid(p.kv_heads, p.mfma_tiles * p.mfma_splits, p.num_units);
+    const bool dealt = p.mfma_splits > 1 && p.num_units * p.mfma_tiles > 1;
+    dim3 grid(p.kv_heads, p.mfma_tiles * p.mfma_splits * (dealt ? p.num_units : 1), dealt ? 1 : p.num_units);
     if (p.mode == kColumn) {
         attn_mfma_kernel<D, Sh::NW, Sh::RT, Sh::BN, Sh::NS, Sh::WPE, false><<<grid, dim3(64 * Sh::NW), 0, stream>>>(p);
     } else {

@@ -88,9 +88,12 @@ __device__ __forceinline__ int32_t vec_unit_blocks(const AttnParams& p, int32_t 
     return b_end > b_first ? b_end - b_first : 0;
 }
 
-// Work groups a unit of nb live blocks gets at bps blocks per work group.
-__device__ __forceinline__ int32_t vec_unit_wgs(int32_t nb, int32_t bps) {
-    return nb < 0 ? 0 : (nb <= bps ? 1 : (nb + bps - 1) / bps);
+// Work groups a unit of nb live blocks gets in a deal of W' work groups over
+// `tot` blocks: max(1, floor(nb * W' / tot)); none for a unit not this path's.
+__device__ __forceinline__ int32_t vec_unit_wgs(int32_t nb, int64_t Wp, int64_t tot) {
+    if (nb < 0) return 0;
+    const int64_t k = tot > 0 ? (int64_t)nb * Wp / tot : 0;
+    return k > 1 ? (int32_t)k : 1;
 }
 
 // Log-sum-exp merge of this lane's (M, tot, o) with lane (lane ^ ST)'s.
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     __shared__ float sLv[kWaves][C::VR][GT];
     __shared__ float sM[kWaves][GT];
     __shared__ int sLast;
-    __shared__ int32_t sWork[5];
+    __shared__ int32_t sWork[4];
 
     // The kv head is the fastest grid dimension: the work groups reading the
     // heads of the same blocks run together and share DRAM rows.
@@ -199,11 +202,12 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     // Which unit and split this work group takes (slot = blockIdx.y):
     //  - one unit: split = slot of num_splits;
     //  - one split per unit: unit = slot;
-    //  - otherwise the units' live blocks are dealt evenly over the
-    //    num_splits * units work groups: bps = ceil(total blocks / work groups),
-    //    and a unit of nb blocks gets ceil(nb / bps) consecutive slots (at
-    //    least one, so that an empty unit still writes its zero row).
-    int32_t u, split, S, slot0, bps = -1;
+    //  - otherwise the num_splits * units slots are dealt over the units in
+    //    proportion to their live blocks: a unit of nb blocks gets
+    //    max(1, floor(nb * W' / total)) consecutive slots (at least one, so an
+    //    empty unit still writes its zero row), W' = slots - units of this
+    //    path, so the deal never needs more slots than that.
+    int32_t u, split, S, slot0;
     if (p.num_units == 1) {
         u = 0; split = slot; S = p.num_splits; slot0 = 0;
     } else if (p.num_splits == 1) {
@@ -215,16 +219,20 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             const int32_t per = (U + 63) / 64;
             const int32_t ub = lane * per, ue = min(U, ub + per);
             int64_t tb = 0;
+            int32_t nv = 0;
             for (int32_t uu = ub; uu < ue; ++uu) {
                 const int32_t nb = vec_unit_blocks(p, uu);
                 tb += nb > 0 ? nb : 0;
+                nv += nb >= 0 ? 1 : 0;
             }
 #pragma unroll
-            for (int st = 1; st < 64; st *= 2) tb += __shfl_xor(tb, st, 64);
-            const int32_t b = (int32_t)((tb + W - 1) / W);
-            const int32_t bp = b > 1 ? b : 1;
+            for (int st = 1; st < 64; st *= 2) {
+                tb += __shfl_xor(tb, st, 64);
+                nv += __shfl_xor(nv, st, 64);
+            }
+            const int64_t Wp = W - nv;
             int32_t cnt = 0;
-            for (int32_t uu = ub; uu < ue; ++uu) cnt += vec_unit_wgs(vec_unit_blocks(p, uu), bp);
+            for (int32_t uu = ub; uu < ue; ++uu) cnt += vec_unit_wgs(vec_unit_blocks(p, uu), Wp, tb);
             int32_t incl = cnt;
 #pragma unroll
             for (int st = 1; st < 64; st *= 2) {
@@ -235,15 +243,15 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             int32_t acc = incl - cnt;
             const int32_t w = slot;
             for (int32_t uu = ub; uu < ue; ++uu) {
-                const int32_t n = vec_unit_wgs(vec_unit_blocks(p, uu), bp);
+                const int32_t n = vec_unit_wgs(vec_unit_blocks(p, uu), Wp, tb);
                 if (w >= acc && w < acc + n) {
-                    sWork[0] = uu; sWork[1] = w - acc; sWork[2] = n; sWork[3] = acc; sWork[4] = bp;
+                    sWork[0] = uu; sWork[1] = w - acc; sWork[2] = n; sWork[3] = acc;
                 }
                 acc += n;
             }
         }
         __syncthreads();
-        u = sWork[0]; split = sWork[1]; S = sWork[2]; slot0 = sWork[3]; bps = sWork[4];
+        u = sWork[0]; split = sWork[1]; S = sWork[2]; slot0 = sWork[3];
         if (u < 0) return;                          // a spare slot
     }
 
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     const int32_t b_end = (hi + 15) >> 4;
     const int32_t b_first = lo >> 4;
     const int32_t nblk = b_end > b_first ? b_end - b_first : 0;
-    if (bps < 0) bps = (nblk + S - 1) / S;
+    const int32_t bps = (nblk + S - 1) / S;
     const int32_t sb = b_first + split * bps;
     const int32_t se = min(b_end, sb + bps);
     int32_t ids = -1;               // lane i: pool block of this wave's i-th block
@@ -645,7 +653,7 @@ int32_t vec_group_rows(int32_t group) {
 int32_t vec_slots(int32_t units, int32_t splits) {
     if (units <= 1) return splits;
     if (splits <= 1) return units;
-    return splits * units + units;
+    return splits * units;
 }
 
 size_t ticket_bytes(int32_t units, int32_t kv_heads) {

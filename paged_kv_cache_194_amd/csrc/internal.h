@@ -106,6 +106,7 @@ hipError_t launch_attn_mfma(const AttnParams& p, pkv_dtype dtype, int32_t head_d
 bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim);
 int32_t mfma_rows_per_group(int32_t head_dim);
 int32_t mfma_chunk_keys(int32_t head_dim);
+int32_t mfma_groups_per_cu(int32_t head_dim);
 
 // Zero every output row of [0, total_q) that no unit covers.
 hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
@@ -122,8 +123,7 @@ constexpr int32_t kTicketStride = 64;
 size_t ticket_bytes(int32_t units, int32_t kv_heads);
 
 // Work-group slots per kv head of the vector path for `units` units at
-// `splits` partitions per unit: the balanced deal over several units can
-// round up once per unit.
+// `splits` partitions per unit.
 int32_t vec_slots(int32_t units, int32_t splits);
 
 }  // namespace pkv
