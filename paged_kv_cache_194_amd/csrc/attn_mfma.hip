@@ -191,10 +191,9 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 
     // Work items are (unit, row tile).  With one split, or one item, slot
     // blockIdx.y of unit blockIdx.z is (tile, split).  Otherwise the
-    // mfma_splits * items slots of a kv head are dealt over the items in
-    // proportion to their chunks: an item of n chunks gets max(1, floor(n * W'
-    // / total)) consecutive slots, W' = slots - items that have work, so the
-    // deal never needs more than the grid holds.
+    // mfma_splits * items slots of a kv head are dealt over the items: an item
+    // of n chunks gets max(1, ceil(n / c)) consecutive slots, c the smallest
+    // chunk count per slot for which the deal fits the grid.
     int32_t u, tile, split, S, slot0;
     if (p.mfma_splits == 1 || p.num_units * T == 1) {
         S = p.mfma_splits;
@@ -207,26 +206,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             const int32_t NI = p.num_units * T;
             const int32_t per = (NI + 63) / 64;
             const int32_t ib = lane * per, ie = min(NI, ib + per);
-            int64_t tot = 0;
-            int32_t valid = 0;
-            for (int32_t it = ib; it < ie; ++it) {
-                const int32_t n = mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN);
-                tot += n > 0 ? n : 0;
-                valid += n >= 0 ? 1 : 0;
-            }
-#pragma unroll
-            for (int st = 1; st < 64; st *= 2) {
-                tot += __shfl_xor(tot, st, 64);
-                valid += __shfl_xor(valid, st, 64);
-            }
-            const int64_t Wp = (int64_t)p.mfma_splits * NI - valid;
-            auto slots_of = [&](int32_t n) -> int32_t {
-                if (n < 0) return 0;
-                const int64_t k = tot > 0 ? (int64_t)n * Wp / tot : 0;
-                return k > 1 ? (int32_t)k : 1;
-            };
+            auto item_n = [&](int32_t it) { return mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN); };
+            const int32_t c = deal_size(item_n, ib, ie, (int64_t)p.mfma_splits * NI);
             int32_t cnt = 0;
-            for (int32_t it = ib; it < ie; ++it) cnt += slots_of(mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN));
+            for (int32_t it = ib; it < ie; ++it) cnt += deal_slots_of(item_n(it), c);
             int32_t incl = cnt;
 #pragma unroll
             for (int st = 1; st < 64; st *= 2) {
@@ -237,7 +220,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             int32_t acc = incl - cnt;
             const int32_t w = blockIdx.y;
             for (int32_t it = ib; it < ie; ++it) {
-                const int32_t k = slots_of(mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN));
+                const int32_t k = deal_slots_of(item_n(it), c);
                 if (w >= acc && w < acc + k) {
                     sWork[0] = it / T; sWork[1] = it - (it / T) * T; sWork[2] = w - acc; sWork[3] = k; sWork[4] = acc;
                 }
@@ -319,42 +302,52 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     const int64_t head_off = (int64_t)g * D * 2;
     int32_t id_base = -kIdWindow;                 // first block of the staged id window
 
-    // Byte offset of key j (head g) in K or V, or -1 when the key is not
-    // wanted (`want` false) or has no storage.  Branch-free: the id window is
-    // read at a clamped index and the checks are selects.
-    auto key_addr = [&](int32_t j, bool want) __attribute__((always_inline)) -> int64_t {
-        if constexpr (PAGED) {
-            int32_t w = (j >> 4) - id_base;
-            w = w < 0 ? 0 : (w >= kIdWindow ? kIdWindow - 1 : w);
-            const int32_t id = sIds[w];
-            const bool ok = want && id >= 0 && id < p.num_blocks;
-            return ok ? ((int64_t)id * 16 + (j & 15)) * tok_stride + head_off : -1;
-        } else {
-            const int32_t r = (j >= 0 ? j : 0) % p.rows;
-            return want ? ((int64_t)r * p.cols + ui.col) * tok_stride + head_off : -1;
-        }
-    };
-
     // Issue chunk c (of this work group's range; past c_end nothing is wanted)
     // into stage st: wave loads w, w + NW, ... of K and of V.  Lane i of wave
     // load I fills stored place I*64 + i of the chunk: row r, stored column cs,
-    // which holds logical column unswz(r, cs) of key c0 + r.
+    // which holds logical column unswz(r, cs) of key c0 + r.  All addresses are
+    // formed first (the block-id reads from LDS then overlap), and only then
+    // are the loads issued.  c0 is a multiple of 16, so key c0 + r lies in
+    // block (c0 >> 4) + (r >> 4) at slot r & 15; a ring row is found from one
+    // modulo per chunk.  A key not wanted, or without storage, reads the zero row.
+    const int64_t blk_stride = 16 * tok_stride;
     auto issue = [&](int32_t c, int st) __attribute__((always_inline)) {
         const int32_t c0 = c_base + c * BN;
         const bool chunk_ok = c < c_end;
         const uint32_t kdst = lds_addr(&sKV[st][0]), vdst = lds_addr(&sKV[st][CB]);
+        int32_t ring0 = 0;
+        if constexpr (!PAGED) ring0 = c0 % p.rows;
+        const uint8_t* ks[IPW];
+        const uint8_t* vs[IPW];
 #pragma unroll
         for (int m = 0; m < IPW; ++m) {
             const int I = wave + NW * m;
             const int place = I * 64 + lane;
             const int r = place / RC, cs = place - (place / RC) * RC;
             const int32_t j = c0 + r;
-            const int64_t a = key_addr(j, chunk_ok && j >= key_lo && j < key_hi);
+            const bool want = chunk_ok && j >= key_lo && j < key_hi;
+            int64_t a;
+            if constexpr (PAGED) {
+                int32_t w = (c0 >> 4) + (r >> 4) - id_base;
+                w = w < 0 ? 0 : (w >= kIdWindow ? kIdWindow - 1 : w);
+                const int32_t id = sIds[w];
+                const bool ok = want && id >= 0 && id < p.num_blocks;
+                a = ok ? (int64_t)id * blk_stride + (r & 15) * tok_stride + head_off : -1;
+            } else {
+                int32_t row = ring0 + r;
+                if (row >= p.rows) row -= p.rows;
+                if (row >= p.rows) row %= p.rows;         // rings shorter than a chunk
+                a = want ? ((int64_t)row * p.cols + ui.col) * tok_stride + head_off : -1;
+            }
             const int off = C::unswz(r, cs) * 16;
-            const uint8_t* ks = a >= 0 ? Kg + a + off : kZeroRow + off;
-            const uint8_t* vs = a >= 0 ? Vg + a + off : kZeroRow + off;
-            dma16(ks, (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024)));
-            dma16(vs, (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024)));
+            ks[m] = a >= 0 ? Kg + a + off : kZeroRow + off;
+            vs[m] = a >= 0 ? Vg + a + off : kZeroRow + off;
+        }
+#pragma unroll
+        for (int m = 0; m < IPW; ++m) {
+            const int I = wave + NW * m;
+            dma16(ks[m], (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024)));
+            dma16(vs[m], (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024)));
         }
     };
     // Stage the block ids of [blk, blk + kIdWindow) (paged): every thread calls it.

@@ -88,13 +88,6 @@ __device__ __forceinline__ int32_t vec_unit_blocks(const AttnParams& p, int32_t 
     return b_end > b_first ? b_end - b_first : 0;
 }
 
-// Work groups a unit of nb live blocks gets in a deal of W' work groups over
-// `tot` blocks: max(1, floor(nb * W' / tot)); none for a unit not this path's.
-__device__ __forceinline__ int32_t vec_unit_wgs(int32_t nb, int64_t Wp, int64_t tot) {
-    if (nb < 0) return 0;
-    const int64_t k = tot > 0 ? (int64_t)nb * Wp / tot : 0;
-    return k > 1 ? (int32_t)k : 1;
-}
 
 // Log-sum-exp merge of this lane's (M, tot, o) with lane (lane ^ ST)'s.
 template <int ST>
@@ -202,11 +195,10 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     // Which unit and split this work group takes (slot = blockIdx.y):
     //  - one unit: split = slot of num_splits;
     //  - one split per unit: unit = slot;
-    //  - otherwise the num_splits * units slots are dealt over the units in
-    //    proportion to their live blocks: a unit of nb blocks gets
-    //    max(1, floor(nb * W' / total)) consecutive slots (at least one, so an
-    //    empty unit still writes its zero row), W' = slots - units of this
-    //    path, so the deal never needs more slots than that.
+    //  - otherwise the num_splits * units slots are dealt over the units: a
+    //    unit of nb live blocks gets max(1, ceil(nb / c)) consecutive slots (at
+    //    least one, so an empty unit still writes its zero row), c the smallest
+    //    block count per slot for which the deal fits the slots.
     int32_t u, split, S, slot0;
     if (p.num_units == 1) {
         u = 0; split = slot; S = p.num_splits; slot0 = 0;
@@ -218,21 +210,10 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             const int64_t W = (int64_t)p.num_splits * U;
             const int32_t per = (U + 63) / 64;
             const int32_t ub = lane * per, ue = min(U, ub + per);
-            int64_t tb = 0;
-            int32_t nv = 0;
-            for (int32_t uu = ub; uu < ue; ++uu) {
-                const int32_t nb = vec_unit_blocks(p, uu);
-                tb += nb > 0 ? nb : 0;
-                nv += nb >= 0 ? 1 : 0;
-            }
-#pragma unroll
-            for (int st = 1; st < 64; st *= 2) {
-                tb += __shfl_xor(tb, st, 64);
-                nv += __shfl_xor(nv, st, 64);
-            }
-            const int64_t Wp = W - nv;
+            auto unit_n = [&](int32_t uu) { return vec_unit_blocks(p, uu); };
+            const int32_t c = deal_size(unit_n, ub, ue, W);
             int32_t cnt = 0;
-            for (int32_t uu = ub; uu < ue; ++uu) cnt += vec_unit_wgs(vec_unit_blocks(p, uu), Wp, tb);
+            for (int32_t uu = ub; uu < ue; ++uu) cnt += deal_slots_of(vec_unit_blocks(p, uu), c);
             int32_t incl = cnt;
 #pragma unroll
             for (int st = 1; st < 64; st *= 2) {
@@ -243,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             int32_t acc = incl - cnt;
             const int32_t w = slot;
             for (int32_t uu = ub; uu < ue; ++uu) {
-                const int32_t n = vec_unit_wgs(vec_unit_blocks(p, uu), Wp, tb);
+                const int32_t n = deal_slots_of(vec_unit_blocks(p, uu), c);
                 if (w >= acc && w < acc + n) {
                     sWork[0] = uu; sWork[1] = w - acc; sWork[2] = n; sWork[3] = acc;
                 }

@@ -150,4 +150,31 @@ __device__ __forceinline__ void lds_barrier() {
 // Wait until every vector memory access this wave issued has completed.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// ---- split-K deal over work items, run by one whole wave ----
+// Lane l owns items [l*per, min(n_items, (l+1)*per)); item_n(i) is the item's
+// work in chunks (>= 0) or -1 when it is not this kernel's.  An item with n
+// chunks takes max(1, ceil(n / c)) consecutive slots; deal_size returns the
+// smallest c for which all items fit into `slots` (binary search; slots must
+// be at least the number of items with work).
+__device__ __forceinline__ int32_t deal_slots_of(int32_t n, int32_t c) {
+    return n < 0 ? 0 : (n <= c ? 1 : (n + c - 1) / c);
+}
+template <typename F>
+__device__ int32_t deal_size(const F& item_n, int32_t ib, int32_t ie, int64_t slots) {
+    int32_t nmax = 0;
+    for (int32_t i = ib; i < ie; ++i) nmax = max(nmax, item_n(i));
+#pragma unroll
+    for (int st = 1; st < 64; st *= 2) nmax = max(nmax, __shfl_xor(nmax, st, 64));
+    int32_t lo = 1, hi = nmax > 1 ? nmax : 1;      // c = nmax gives one slot per item
+    while (lo < hi) {                              // wave-uniform loop
+        const int32_t c = lo + (hi - lo) / 2;
+        int64_t k = 0;
+        for (int32_t i = ib; i < ie; ++i) k += deal_slots_of(item_n(i), c);
+#pragma unroll
+        for (int st = 1; st < 64; st *= 2) k += __shfl_xor(k, st, 64);
+        if (k <= slots) hi = c; else lo = c + 1;
+    }
+    return lo;
+}
+
 }  // namespace pkv
