@@ -113,9 +113,15 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  * softmax_scale: multiplies q.k before the softmax.
  * causal       : with one query per sequence causal equals non-causal.
  * window       : > 0 keeps the last `window` keys (p - window + 1 .. p).
- * num_splits   : split-K partitions per (sequence, kv head); 0 lets the library
- *                pick from the host arguments.  Results of different split counts
- *                agree to rounding; a fixed split count is deterministic.
+ * num_splits   : split-K partitions per (sequence, kv head) on average; 0 lets the
+ *                library pick from the host arguments.  With one sequence the
+ *                live keys are cut into num_splits ranges; with several, the
+ *                num_splits * num_seqs work groups of a kv head are dealt over the
+ *                sequences by live length (on the device), so a long sequence
+ *                takes more of them.  Results of different split counts agree to
+ *                rounding; the same inputs and split count give the same bits.
+ *                The library's own choice depends on the current device's
+ *                compute-unit count for multi-row units.
  * workspace    : device scratch of at least pkv_attn_workspace_bytes(num_seqs, 1,
  *                max_seqlen_k, q_heads, kv_heads, head_dim, num_splits) bytes
  *                (may be NULL when that is 0).  Zero-fill it once before its
@@ -173,7 +179,9 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q,
 /*
  * pkv_attn_workspace_bytes -- device scratch an attention call with these host
  * arguments needs (split-K partials); 0 when it needs none.  `units` is num_seqs
- * (paged) or num_segments (column); num_splits as passed to the call.
+ * (paged) or num_segments (column); num_splits as passed to the call.  With
+ * num_splits = 0 the answer depends on the current device (its compute-unit
+ * count), so ask with the device current that will run the call.
  */
 size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim,
