@@ -122,3 +122,47 @@ def test_varlen_single_and_multi_row_units_mixed():
                         num_splits=splits)
         torch.cuda.synchronize()
         check_close(out, oracle_paged(inp), "bf16", f"mixed varlen splits={splits}")
+
+
+def _mixed_call(inp, out, ws, splits=0):
+    pkv.varlen_attn(out, inp.q, inp.k_cache, inp.v_cache, cu_seqlens_q=inp.cu_seqlens_q,
+                    seqused_k=inp.seqused_k, block_table=inp.block_table, max_seqlen_q=16,
+                    max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale, causal=True,
+                    num_splits=splits, workspace=ws)
+
+
+def _mixed_inputs():
+    return workloads.paged_inputs(seed=760, lengths=[900, 40, 0, 3000, 300, 17, 1200], q_lens=[1, 4, 1, 1, 7, 1, 16],
+                                  q_heads=32, kv_heads=8, head_dim=128, dtype=torch.bfloat16, num_blocks=400,
+                                  max_blocks=200, causal=True, device=DEV)
+
+
+def _capture_and_replay(inp, label):
+    """Capture one mixed call, replay it three times with eager work between
+    the replays; every replay must equal the eager result bit for bit."""
+    ws = torch.zeros(pkv.attn_workspace_bytes(7, 16, inp.max_seqlen_k, 32, 8, 128, 0), dtype=torch.uint8,
+                     device=DEV)
+    eager = torch.full_like(inp.q, float("nan"))
+    _mixed_call(inp, eager, ws)
+    torch.cuda.synchronize()
+    out = torch.full_like(inp.q, float("nan"))
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            _mixed_call(inp, out, ws)
+    for k in range(3):
+        out.fill_(float("nan"))
+        scratch = torch.full_like(inp.q, float("nan"))
+        _mixed_call(inp, scratch, ws)                 # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"{label}: replay {k} != eager"
+    check_close(out, oracle_paged(inp), "bf16", label)
+
+
+def test_graph_of_mixed_call_replays_like_eager():
+    """One-row and multi-row units in one call (vector and matrix-core kernels,
+    zeroed rows) captured once and replayed with eager work in between."""
+    _capture_and_replay(_mixed_inputs(), "mixed call in a graph")
