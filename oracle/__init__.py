@@ -20,6 +20,9 @@ without blocking, splitting or fusion:
   start+T keys sees keys 0..start+i); the ``sdpa_varlen`` segment table,
   sliding window, ring storage and zeroed uncovered rows of ExecuTorch PR
   #24073 (the #24072 part).
+* prefix import / export -- ``PagedDecodeCache.load_prefix``,
+  ``_write_prefix`` and ``to_dynamic_cache``: a dense prefill cache
+  ``[B, Hkv, S, D]`` to and from the slots of the paged cache, raw bits.
 
 Readings taken where the pages are silent (each is also listed with its
 support in the design notes):
@@ -34,7 +37,9 @@ support in the design notes):
 * a live key whose block-table entry lies outside ``[0, num_blocks)``, or a
   segment whose column lies outside ``[0, cols)``, contributes no keys;
 * query rows of a unit past ``max_seqlen_q`` are treated as uncovered (0);
-* ``kv_append`` skips slots outside ``[0, num_slots)`` and copies raw bits.
+* ``kv_append`` skips slots outside ``[0, num_slots)`` and copies raw bits;
+* prefix import takes the same rule; prefix export writes zero bits for a
+  position whose slot lies outside the cache.
 """
 from __future__ import annotations
 
@@ -322,6 +327,57 @@ def column_attention(q, k_store, v_store, seq_info, *, dtype: str, scale: float,
             if 0 <= r < total_q:
                 out[r] = res[i]
     return out
+
+
+# --------------------------------------------------------------------------
+# Prefix import / export between a dense prefill cache and paged slots.
+# --------------------------------------------------------------------------
+
+
+def prefix_import(k_flat: np.ndarray, v_flat: np.ndarray, k_src: np.ndarray,
+                  v_src: np.ndarray, block_table: np.ndarray,
+                  n: int) -> tuple[np.ndarray, np.ndarray]:
+    """vLLM-Omni ``paged_decode.py``, ``PagedDecodeCache.load_prefix`` and
+    ``_write_prefix``: a prefill cache holds, per sequence, one ``[S, D]`` plane
+    per kv head (``[B, Hkv, S, D]``); its first ``n`` positions are written into
+    the paged cache position by position, position ``j`` of sequence ``b``
+    (all heads: ``src[b, :, j, :]``) going to the slot its block-table row
+    names.  The pages copy into the flat view through an identity table; any
+    table reads the same way.
+
+    Arrays are integer bit views, so every bit is moved untouched.  A position
+    whose slot lies outside ``[0, num_slots)`` is skipped, and every slot not
+    written keeps its old contents (the pages leave the tail stale).  Returns
+    copies of the flat caches ``[num_slots, Hkv, D]``.
+    """
+    k_out = np.array(k_flat, copy=True)
+    v_out = np.array(v_flat, copy=True)
+    num_slots = k_out.shape[0]
+    for b in range(k_src.shape[0]):
+        for j in range(n):
+            s = paged_slot(block_table[b], j)
+            if 0 <= s < num_slots:
+                k_out[s] = k_src[b, :, j, :]
+                v_out[s] = v_src[b, :, j, :]
+    return k_out, v_out
+
+
+def prefix_export(k_flat: np.ndarray, v_flat: np.ndarray, block_table: np.ndarray,
+                  batch: int, n: int) -> tuple[np.ndarray, np.ndarray]:
+    """``PagedDecodeCache.to_dynamic_cache``: the first ``n`` positions of each
+    sequence read back out of the paged cache into a dense ``[B, Hkv, n, D]``
+    cache (``out[b, :, j, :]`` is the slot row of position ``j``).  A position
+    whose slot lies outside the cache reads as all-zero bits."""
+    num_slots, H, D = k_flat.shape
+    k_out = np.zeros((batch, H, n, D), dtype=k_flat.dtype)
+    v_out = np.zeros((batch, H, n, D), dtype=v_flat.dtype)
+    for b in range(batch):
+        for j in range(n):
+            s = paged_slot(block_table[b], j)
+            if 0 <= s < num_slots:
+                k_out[b, :, j, :] = k_flat[s]
+                v_out[b, :, j, :] = v_flat[s]
+    return k_out, v_out
 
 
 # --------------------------------------------------------------------------

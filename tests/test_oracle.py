@@ -491,6 +491,79 @@ def pin_bf16_decode():
     assert np.array_equal(oracle.to_f64(rnd, "bf16"), f64(rnd, "bf16"))
 
 
+def pin_golden_prefix_copy():
+    """Hand-worked import through a permuted table, a block edge crossed at
+    position 16, a tail past n left alone, and a sequence whose table names no
+    pool block; the export reads the same values back (zero for that one)."""
+    fx = _load("prefix_copy.json")
+    H, D, S, n, nb = fx["kv_heads"], fx["head_dim"], fx["src_len"], fx["n"], fx["num_blocks"]
+    bt = np.array(fx["block_table"], dtype=np.int32)
+    B = bt.shape[0]
+    b, h, j, d = np.meshgrid(np.arange(B), np.arange(H), np.arange(S), np.arange(D), indexing="ij")
+    k_src = (1000 * b + 100 * h + 10 * j + d).astype(np.uint32)
+    v_src = k_src + np.uint32(fx["v_offset"])
+    fill = np.uint32(0xDEADBEEF)
+    k_flat = np.full((nb * 16, H, D), fill, dtype=np.uint32)
+    v_flat = np.full((nb * 16, H, D), fill, dtype=np.uint32)
+    ko, vo = oracle.prefix_import(k_flat, v_flat, k_src, v_src, bt, n)
+    hh, dd = np.meshgrid(np.arange(H), np.arange(D), indexing="ij")
+    for sb, sj, slot in fx["written"]:
+        want = 1000 * sb + 100 * hh + 10 * sj + dd
+        assert np.array_equal(ko[slot], want) and np.array_equal(vo[slot], want + fx["v_offset"])
+    for slot in fx["untouched_slots"]:
+        assert (ko[slot] == fill).all() and (vo[slot] == fill).all()
+    written = {slot for _, _, slot in fx["written"]}
+    assert len(written) == len(fx["written"])
+    ke, ve = oracle.prefix_export(ko, vo, bt, B, n)
+    assert ke.shape == (B, H, n, D)
+    for sb in range(B):
+        if sb in fx["skipped_sequences"]:
+            assert (ke[sb] == 0).all() and (ve[sb] == 0).all()
+        else:
+            assert np.array_equal(ke[sb], k_src[sb, :, :n]) and np.array_equal(ve[sb], v_src[sb, :, :n])
+
+
+def pin_prefix_identity_is_transpose():
+    """With one sequence and the identity table the import is the pages' flat
+    copy of the [S, H, D] transpose into slots [:n], and the export the
+    transpose back of slots [:n]; bf16 bit patterns including NaN payloads."""
+    rng = np.random.default_rng(31)
+    H, D, S, n = 3, 16, 45, 37
+    k_src = rng.integers(0, 1 << 16, size=(1, H, S, D)).astype(np.uint16)
+    v_src = rng.integers(0, 1 << 16, size=(1, H, S, D)).astype(np.uint16)
+    k_src[0, 1, 3, :4] = [0x7FC1, 0xFF81, 0x7F80, 0x8000]
+    k_flat = rng.integers(0, 1 << 16, size=(64, H, D)).astype(np.uint16)
+    v_flat = rng.integers(0, 1 << 16, size=(64, H, D)).astype(np.uint16)
+    ident = np.arange(4, dtype=np.int32)[None, :]
+    ko, vo = oracle.prefix_import(k_flat, v_flat, k_src, v_src, ident, n)
+    assert np.array_equal(ko[:n], np.transpose(k_src[0], (1, 0, 2))[:n])
+    assert np.array_equal(vo[:n], np.transpose(v_src[0], (1, 0, 2))[:n])
+    assert np.array_equal(ko[n:], k_flat[n:]) and np.array_equal(vo[n:], v_flat[n:])
+    ke, ve = oracle.prefix_export(ko, vo, ident, 1, n)
+    assert np.array_equal(ke, np.ascontiguousarray(np.transpose(ko[:n], (1, 0, 2)))[None])
+    assert np.array_equal(ve, np.ascontiguousarray(np.transpose(vo[:n], (1, 0, 2)))[None])
+
+
+def pin_prefix_roundtrip_permuted():
+    """Three sequences on disjoint permuted pool blocks: export after import
+    gives back the first n source positions, and exactly the slots the tables
+    name for positions < n changed (the test finds them by comparing)."""
+    rng = np.random.default_rng(32)
+    B, H, D, S, n, nb = 3, 2, 8, 50, 41, 20
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = perm[:B * 4].reshape(B, 4)
+    k_src = rng.integers(0, 1 << 32, size=(B, H, S, D), dtype=np.uint64).astype(np.uint32)
+    v_src = rng.integers(0, 1 << 32, size=(B, H, S, D), dtype=np.uint64).astype(np.uint32)
+    k_flat = np.zeros((nb * 16, H, D), dtype=np.uint32) + np.uint32(7)
+    v_flat = k_flat.copy()
+    ko, vo = oracle.prefix_import(k_flat, v_flat, k_src, v_src, bt, n)
+    ke, ve = oracle.prefix_export(ko, vo, bt, B, n)
+    assert np.array_equal(ke, k_src[:, :, :n]) and np.array_equal(ve, v_src[:, :, :n])
+    changed = np.flatnonzero((ko != 7).any(axis=(1, 2)))
+    expect = sorted(int(bt[b, j // 16]) * 16 + j % 16 for b in range(B) for j in range(n))
+    assert changed.tolist() == expect
+
+
 ALL_PINS = [
     pin_bf16_decode,
     pin_golden_causal_rule, pin_golden_slots, pin_golden_closed_forms, pin_window_span,
@@ -498,6 +571,7 @@ ALL_PINS = [
     pin_window1_gather, pin_single_key, pin_permutation_invariance, pin_garbage_invariance,
     pin_uncovered_rows_zero, pin_window_large_is_none, pin_ring_equals_unrolled, pin_gqa_repeat,
     pin_closed_form_means, pin_kv_append_bits,
+    pin_golden_prefix_copy, pin_prefix_identity_is_transpose, pin_prefix_roundtrip_permuted,
 ]
 
 
@@ -564,6 +638,33 @@ def _attend_last_kv_head(q, keys, vals, ok, E, scale, causal, window, chunk=64):
 _real_ring = oracle.ring_slot
 
 
+_real_import = oracle.prefix_import
+_real_export = oracle.prefix_export
+
+
+def _import_heads_reversed(kf, vf, ks, vs, bt, n):
+    return _real_import(kf, vf, ks[:, ::-1], vs[:, ::-1], bt, n)
+
+
+def _import_kv_swapped(kf, vf, ks, vs, bt, n):
+    return _real_import(kf, vf, vs, ks, bt, n)
+
+
+def _import_one_extra(kf, vf, ks, vs, bt, n):
+    return _real_import(kf, vf, ks, vs, bt, min(n + 1, ks.shape[2]))
+
+
+def _import_s_h_mixed(kf, vf, ks, vs, bt, n):
+    B, H, S, D = ks.shape
+    return _real_import(kf, vf, ks.reshape(B, S, H, D).transpose(0, 2, 1, 3),
+                        vs.reshape(B, S, H, D).transpose(0, 2, 1, 3), bt, n)
+
+
+def _export_shifted(kf, vf, bt, B, n):
+    ke, ve = _real_export(kf, vf, bt, B, n + 1)
+    return ke[:, :, 1:], ve[:, :, 1:]
+
+
 MUTANTS = [
     ("visible_range", _top_left_causal),
     ("visible_range", _window_off_by_one),
@@ -576,6 +677,12 @@ MUTANTS = [
     ("ring_slot", lambda p, rows, cols, col: (p % rows) + col * rows),
     ("bf16_bits_to_f64", lambda b: (np.asarray(b).astype(np.uint32) << 15).view(np.float32)
      .astype(np.float64)),
+    ("prefix_import", _import_heads_reversed),
+    ("prefix_import", _import_kv_swapped),
+    ("prefix_import", _import_one_extra),
+    ("prefix_import", _import_s_h_mixed),
+    ("prefix_export", _export_shifted),
+    ("paged_slot", lambda row, j: int(row[j // 16]) * 16 + 15 - j % 16),
 ]
 
 
