@@ -17,8 +17,10 @@ Printed on one JSON line:
                  replays of 42 back-to-back calls, against 8 TB/s HBM;
   cpu_baseline   the fp64 CPU oracle on the same step's bits, timed on the host.
 
-Other workloads (--config c3 / c4 / c5) print the same kind of line for the
-64-sequence batched decode, the column-store step and the long-context passes.
+Other workloads (--config c3 / c4 / c5 / c5d) print the same kind of line for
+the 64-sequence batched decode, the column-store step and the long-context
+passes; --config prefix times the prefill hand-over copies (import of a
+4096-token prefill cache into every layer, export back out).
 """
 from __future__ import annotations
 
@@ -301,6 +303,102 @@ def bench_single_call(args, torch):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
 
 
+def bench_prefix(args, torch):
+    """Prefill hand-over of the 42-layer decode model: every layer's 4096-token
+    [1, 8, 4096, 128] bf16 prefill K/V imported into an 8192 bucket (identity
+    table), then the same 4096 positions exported back to dense tensors.  One
+    step = 84 copy launches in one graph; bytes = what the copies must read and
+    write (4 x 704.6 MB)."""
+    import numpy as np
+
+    import paged_kv_cache_194_amd as pkv
+    import workloads
+    from paged_kv_cache_194_amd.harness import PagedDecodeCache
+
+    m = workloads.DecodeModel()
+    n = args.ctx
+    dev = torch.device("cuda:0")
+    keys = [workloads.randn((1, m.kv_heads, n, m.head_dim), m.dtype, workloads.SEED_BASE + 300 + i, dev)
+            for i in range(m.layers)]
+    vals = [workloads.randn((1, m.kv_heads, n, m.head_dim), m.dtype, workloads.SEED_BASE + 400 + i, dev)
+            for i in range(m.layers)]
+    cache = PagedDecodeCache(m.layers, m.q_heads, m.kv_heads, m.head_dim, n + 1, dev, m.dtype)
+    k_out = [torch.empty_like(k) for k in keys]
+    v_out = [torch.empty_like(v) for v in vals]
+
+    def import_all():
+        for i in range(m.layers):
+            pkv.prefix_import(cache.k[i], cache.v[i], keys[i], vals[i], cache.block_table, n,
+                              seqused_k=cache.seqused if i == m.layers - 1 else None)
+
+    def export_all():
+        for i in range(m.layers):
+            pkv.prefix_export(k_out[i], v_out[i], cache.k[i], cache.v[i], cache.block_table)
+
+    def step():
+        import_all()
+        export_all()
+
+    layer_bytes = 2 * n * m.kv_heads * m.head_dim * 2          # K + V of one layer
+    step_bytes = 4 * m.layers * layer_bytes                      # import r+w, export r+w
+    g = capture(torch, step)
+    time_graph(torch, g, max(1, args.warmup))
+    t_wall0 = time.perf_counter()
+    sec = time_graph(torch, g, args.steps)
+    wall = time.perf_counter() - t_wall0
+    for i in (0, m.layers - 1):     # a cheap end-to-end check on the last replay
+        if not (torch.equal(k_out[i].view(torch.int16), keys[i].view(torch.int16))
+                and torch.equal(v_out[i].view(torch.int16), vals[i].view(torch.int16))):
+            raise SystemExit(f"prefix round trip differs at layer {i}")
+    g_imp, g_exp = capture(torch, import_all), capture(torch, export_all)
+    reps = max(5, args.steps // 2)
+    time_graph(torch, g_imp, 2)
+    sec_imp = time_graph(torch, g_imp, reps) / m.layers
+    time_graph(torch, g_exp, 2)
+    sec_exp = time_graph(torch, g_exp, reps) / m.layers
+    per_launch = 2 * layer_bytes                                 # read + write of one call
+    gbs = step_bytes / sec / 1e9
+    name = "prefix import + export, 42 layers x [1, 8, 4096, 128] bf16, identity table"
+    res = {"metric": "prefill hand-over copy GB/s (import + export)", "value": round(gbs, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(sec * 1e3, 5), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": name, "layers": m.layers, "positions": n, "kv_heads": m.kv_heads,
+                      "head_dim": m.head_dim, "bytes_per_step": step_bytes},
+           "roofline": {"bound": "hbm", "achieved": round(per_launch / sec_imp / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(per_launch / sec_imp / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": traffic_from_profiles("prefix_import_4k"),
+                        "kernel": "prefix_import call (one layer, 4096 positions)",
+                        "bytes_per_launch": per_launch, "us_per_launch": round(sec_imp * 1e6, 3)},
+           "roofline_export": {"bound": "hbm", "achieved": round(per_launch / sec_exp / 1e9, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(per_launch / sec_exp / 1e9 / HBM_PEAK_GBS, 4),
+                               "us_per_launch": round(sec_exp * 1e6, 3)},
+           "wall_s_timed": round(wall, 4)}
+    if args.copy_ceiling:
+        res["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
+    if not args.no_cpu_baseline:
+        import oracle
+        layers = list(range(min(m.layers, args.cpu_layers)))
+        host = [(keys[i].cpu().view(torch.int16).numpy(), vals[i].cpu().view(torch.int16).numpy(),
+                 cache.k[i].cpu().view(torch.int16).numpy().reshape(-1, m.kv_heads, m.head_dim),
+                 cache.v[i].cpu().view(torch.int16).numpy().reshape(-1, m.kv_heads, m.head_dim))
+                for i in layers]
+        bt = cache.block_table.cpu().numpy()
+        t0 = time.perf_counter()
+        for ks, vs, kc, vc in host:
+            ki, vi = oracle.prefix_import(kc, vc, ks, vs, bt, n)
+            oracle.prefix_export(ki, vi, bt, 1, n)
+        csec = (time.perf_counter() - t0) / len(layers) * m.layers
+        res["cpu_baseline"] = {"value": round(step_bytes / csec / 1e9, 4), "unit": "GB/s",
+                               "cores": cpu_threads(), "kind": "oracle", "sec_per_step": round(csec, 3),
+                               "sample": f"import + export of {len(layers)} of {m.layers} layers, "
+                                         "scaled to the step"}
+    return res
+
+
 def visible_pairs(E: int, L: int, causal: bool, window: int):
     """(union of visible keys, number of visible (query, key) pairs) of one unit."""
     lo_u, hi_u, pairs = None, 0, 0
@@ -387,7 +485,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c5d"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c5d", "prefix"])
     ap.add_argument("--ctx", type=int, default=4096, help="live keys of the 42-layer decode step")
     ap.add_argument("--splits", type=int, default=0, help="split-K partitions (0: library choice)")
     ap.add_argument("--cpu-layers", type=int, default=42, help="layers the CPU oracle times")
@@ -405,7 +503,12 @@ def main():
         sys.exit(1)
     import paged_kv_cache_194_amd as pkv
     pkv.lib()        # fail loudly if the library is missing
-    res = bench_decode_step(args, torch) if args.config == "c2" else bench_single_call(args, torch)
+    if args.config == "c2":
+        res = bench_decode_step(args, torch)
+    elif args.config == "prefix":
+        res = bench_prefix(args, torch)
+    else:
+        res = bench_single_call(args, torch)
     print(json.dumps(res), flush=True)
 
 

@@ -1,6 +1,7 @@
 /*
  * pagedkv.h -- C ABI of libpagedkv.so: K/V append and varlen decode attention
- * over a paged KV cache or a column-packed ring store, for AMD gfx950.
+ * over a paged KV cache or a column-packed ring store, and the prefix copies
+ * between a dense prefill cache and the paged one, for AMD gfx950.
  *
  * Sources of the operations (pages, by title and section):
  *  - vLLM-Omni "paged_decode" (SenseNova-U1), PagedDecodeCache class docstring
@@ -175,6 +176,57 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q,
                            float softmax_scale, int32_t causal, int32_t window,
                            int32_t num_splits, void* workspace, size_t workspace_bytes,
                            pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_prefix_import -- copy the first n positions of a dense prefill cache into
+ * the paged cache and, optionally, set the live length to n.
+ * (vLLM-Omni paged_decode, PagedDecodeCache.load_prefix and _write_prefix: the
+ * [B, kv_heads, S, head_dim] prefill K/V of a layer, taken as one
+ * [kv_heads, head_dim] row per position, written into the cache slots, then
+ * set_length(prefix); from_dynamic_cache sizes the bucket for prefix + 1.)
+ *
+ * k_cache, v_cache : [num_blocks, 16, kv_heads, head_dim], written in place.
+ * k_src, v_src     : [batch, kv_heads, src_len, head_dim], read only.
+ * block_table      : int32 [batch, max_blocks_per_seq]; position j of sequence b
+ *                    goes to slot 16 * block_table[b][j / 16] + j % 16.  A
+ *                    position whose entry lies outside [0, num_blocks) is skipped;
+ *                    entries past ceil(n / 16) are never read.
+ * n                : positions copied per sequence; 0 <= n <= src_len and
+ *                    n <= 16 * max_blocks_per_seq.
+ * seqused_k        : optional int32 [batch]; when non-NULL every entry is set to n
+ *                    by the same launch (set_length), so a following attention
+ *                    call on the stream sees the imported prefix as live.
+ * Raw 16/32-bit words are moved (NaN payloads arrive unchanged).  Slots not
+ * written keep their contents: the tail past n is left as it was.  Two positions
+ * whose tables name the same slot leave that slot undefined.  All four tensor
+ * pointers must be 16-byte aligned (PKV_EINVAL otherwise).  batch == 0, or
+ * n == 0 without seqused_k, enqueues nothing.
+ */
+pkv_status pkv_prefix_import(void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size,
+                             const void* k_src, const void* v_src, int32_t batch, int32_t src_len,
+                             int32_t n, const int32_t* block_table, int32_t max_blocks_per_seq,
+                             int32_t* seqused_k, int32_t kv_heads, int32_t head_dim,
+                             pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_prefix_export -- copy the first n positions of each sequence out of the
+ * paged cache into a dense cache.
+ * (vLLM-Omni paged_decode, PagedDecodeCache.to_dynamic_cache: slots [:n] as a
+ * contiguous [1, kv_heads, n, head_dim] for the stage that reads an ordinary
+ * cache, once at hand-off.)
+ *
+ * k_dst, v_dst     : [batch, kv_heads, n, head_dim], every element written.
+ * k_cache, v_cache : [num_blocks, 16, kv_heads, head_dim], read only.
+ * block_table, n   : as for pkv_prefix_import (here src_len is n).  A position
+ *                    whose entry lies outside [0, num_blocks) is written as zero
+ *                    bits.
+ * Raw words are moved; pointers must be 16-byte aligned.  batch == 0 or n == 0
+ * enqueues nothing.
+ */
+pkv_status pkv_prefix_export(void* k_dst, void* v_dst, const void* k_cache, const void* v_cache,
+                             int32_t num_blocks, int32_t block_size, int32_t batch, int32_t n,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             int32_t kv_heads, int32_t head_dim, pkv_dtype dtype, void* stream);
 
 /*
  * pkv_attn_workspace_bytes -- device scratch an attention call with these host

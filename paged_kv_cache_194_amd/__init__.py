@@ -16,8 +16,8 @@ import torch
 
 __all__ = [
     "PagedKVError", "BLOCK_SIZE", "lib", "library_path", "kv_append", "paged_decode_attn",
-    "varlen_attn", "attn_workspace_bytes", "attn_num_splits", "status_string", "last_error",
-    "EXPORTED_SYMBOLS",
+    "varlen_attn", "prefix_import", "prefix_export", "attn_workspace_bytes", "attn_num_splits",
+    "status_string", "last_error", "EXPORTED_SYMBOLS",
 ]
 
 BLOCK_SIZE = 16
@@ -28,8 +28,9 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTED_SYMBOLS = (
-    "pkv_kv_append", "pkv_paged_decode_attn", "pkv_varlen_attn", "pkv_attn_workspace_bytes",
-    "pkv_attn_num_splits", "pkv_status_string", "pkv_last_error",
+    "pkv_kv_append", "pkv_paged_decode_attn", "pkv_varlen_attn", "pkv_prefix_import",
+    "pkv_prefix_export", "pkv_attn_workspace_bytes", "pkv_attn_num_splits", "pkv_status_string",
+    "pkv_last_error",
 )
 
 
@@ -57,6 +58,10 @@ _SIGS = {
     "pkv_varlen_attn": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                _i32, _i32, _vp, _sz, _i32, _vp]),
+    "pkv_prefix_import": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
+                                 _i32, _i32, _i32, _vp]),
+    "pkv_prefix_export": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32,
+                                 _i32, _vp]),
     "pkv_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_attn_num_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -133,6 +138,53 @@ def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
     num_slots = k_cache.numel() // (H * D)
     _check(lib().pkv_kv_append(_ptr(k_cache), _ptr(v_cache), num_slots, _ptr(k_new), _ptr(v_new),
                                T, _ptr(slot_mapping), H, D, _dtype(k_new), _stream(k_new)))
+
+
+def _paged_cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    _need(k_cache.dim() == 4 and k_cache.shape[1] == BLOCK_SIZE,
+          "paged caches must be [num_blocks, 16, Hkv, D]")
+    _need(k_cache.shape == v_cache.shape and k_cache.dtype == v_cache.dtype,
+          "k_cache and v_cache differ in shape or dtype")
+    return k_cache.shape[0], k_cache.shape[2], k_cache.shape[3]
+
+
+def prefix_import(k_cache: torch.Tensor, v_cache: torch.Tensor, k_src: torch.Tensor,
+                  v_src: torch.Tensor, block_table: torch.Tensor, n: Optional[int] = None,
+                  seqused_k: Optional[torch.Tensor] = None) -> None:
+    """Copy positions ``[:n]`` (default: all) of a dense prefill cache
+    ``[B, Hkv, S, D]`` into the paged caches through ``block_table`` ``[B, M]``;
+    when ``seqused_k`` ``[B]`` is given it is set to ``n`` by the same launch."""
+    _dev(k_cache, v_cache, k_src, v_src, block_table, seqused_k)
+    nb, H, D = _paged_cache_dims(k_cache, v_cache)
+    _need(k_src.dim() == 4 and k_src.shape == v_src.shape, "k_src/v_src must be [B, Hkv, S, D]")
+    _need(k_src.dtype == v_src.dtype == k_cache.dtype, "dtypes differ")
+    B, Hs, S, Ds = k_src.shape
+    _need((Hs, Ds) == (H, D), "source heads / head_dim differ from the cache")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+          "block_table must be int32 [B, max_blocks]")
+    if seqused_k is not None:
+        _need(seqused_k.dtype == torch.int32 and seqused_k.numel() == B, "seqused_k must be int32 [B]")
+    n = S if n is None else int(n)
+    _check(lib().pkv_prefix_import(_ptr(k_cache), _ptr(v_cache), nb, BLOCK_SIZE, _ptr(k_src),
+                                   _ptr(v_src), B, S, n, _ptr(block_table), block_table.shape[1],
+                                   _ptr(seqused_k), H, D, _dtype(k_cache), _stream(k_cache)))
+
+
+def prefix_export(k_dst: torch.Tensor, v_dst: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, block_table: torch.Tensor) -> None:
+    """Copy the first ``n`` positions of each sequence out of the paged caches
+    into dense ``k_dst``/``v_dst`` ``[B, Hkv, n, D]``."""
+    _dev(k_dst, v_dst, k_cache, v_cache, block_table)
+    nb, H, D = _paged_cache_dims(k_cache, v_cache)
+    _need(k_dst.dim() == 4 and k_dst.shape == v_dst.shape, "k_dst/v_dst must be [B, Hkv, n, D]")
+    _need(k_dst.dtype == v_dst.dtype == k_cache.dtype, "dtypes differ")
+    B, Hd, n, Dd = k_dst.shape
+    _need((Hd, Dd) == (H, D), "destination heads / head_dim differ from the cache")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+          "block_table must be int32 [B, max_blocks]")
+    _check(lib().pkv_prefix_export(_ptr(k_dst), _ptr(v_dst), _ptr(k_cache), _ptr(v_cache), nb,
+                                   BLOCK_SIZE, B, n, _ptr(block_table), block_table.shape[1], H, D,
+                                   _dtype(k_cache), _stream(k_cache)))
 
 
 def attn_workspace_bytes(units: int, max_seqlen_q: int, max_seqlen_k: int, q_heads: int,

@@ -199,6 +199,73 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots, const 
                       "kv_append");
 }
 
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Shared checks of the two prefix copies; fills row_bytes on success.
+pkv_status check_prefix(int32_t num_blocks, int32_t block_size, int32_t batch, int32_t n,
+                        int32_t max_blocks_per_seq, int32_t kv_heads, int32_t head_dim,
+                        pkv_dtype dtype, int64_t* row_bytes) {
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "unknown dtype %d", (int)dtype);
+    if (block_size != PKV_BLOCK_SIZE) return fail(PKV_EINVAL, "block_size %d: must be 16", block_size);
+    if (kv_heads <= 0 || head_dim <= 0 || head_dim % 8 != 0)
+        return fail(PKV_EINVAL, "kv_heads must be > 0 and head_dim a positive multiple of 8");
+    if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+        return fail(PKV_EINVAL, "num_blocks and max_blocks_per_seq must be > 0");
+    if (batch < 0 || n < 0) return fail(PKV_EINVAL, "batch and n must be >= 0");
+    if ((int64_t)n > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+        return fail(PKV_EINVAL, "n = %d exceeds 16 * max_blocks_per_seq", n);
+    *row_bytes = (int64_t)head_dim * elem_bytes(dtype);
+    // One work group per (sequence, block of 16 positions); 32-bit chunk index.
+    if ((int64_t)batch * ((n + 15) / 16) >= ((int64_t)1 << 24) ||
+        (int64_t)16 * kv_heads * (*row_bytes / 16) >= ((int64_t)1 << 30))
+        return fail(PKV_EINVAL, "prefix copy too large for one launch");
+    return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status pkv_prefix_import(void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size,
+                             const void* k_src, const void* v_src, int32_t batch, int32_t src_len,
+                             int32_t n, const int32_t* block_table, int32_t max_blocks_per_seq,
+                             int32_t* seqused_k, int32_t kv_heads, int32_t head_dim,
+                             pkv_dtype dtype, void* stream) {
+    int64_t row_bytes = 0;
+    pkv_status s = check_prefix(num_blocks, block_size, batch, n, max_blocks_per_seq, kv_heads,
+                                head_dim, dtype, &row_bytes);
+    if (s != PKV_OK) return s;
+    if (src_len < n) return fail(PKV_EINVAL, "src_len %d < n %d", src_len, n);
+    if (batch == 0 || (n == 0 && !seqused_k)) return ok();
+    if (n > 0 && (!k_cache || !v_cache || !k_src || !v_src || !block_table))
+        return fail(PKV_EINVAL, "null pointer argument");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_src) || !aligned16(v_src))
+        return fail(PKV_EINVAL, "cache and source pointers must be 16-byte aligned");
+    return hip_status(pkv::launch_prefix_copy(false, k_cache, v_cache, k_src, v_src, block_table,
+                                              max_blocks_per_seq, num_blocks, batch, n, src_len,
+                                              kv_heads, row_bytes, seqused_k, (hipStream_t)stream),
+                      "prefix_import");
+}
+
+pkv_status pkv_prefix_export(void* k_dst, void* v_dst, const void* k_cache, const void* v_cache,
+                             int32_t num_blocks, int32_t block_size, int32_t batch, int32_t n,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             int32_t kv_heads, int32_t head_dim, pkv_dtype dtype, void* stream) {
+    int64_t row_bytes = 0;
+    pkv_status s = check_prefix(num_blocks, block_size, batch, n, max_blocks_per_seq, kv_heads,
+                                head_dim, dtype, &row_bytes);
+    if (s != PKV_OK) return s;
+    if (batch == 0 || n == 0) return ok();
+    if (!k_dst || !v_dst || !k_cache || !v_cache || !block_table)
+        return fail(PKV_EINVAL, "null pointer argument");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_dst) || !aligned16(v_dst))
+        return fail(PKV_EINVAL, "cache and destination pointers must be 16-byte aligned");
+    return hip_status(pkv::launch_prefix_copy(true, k_dst, v_dst, k_cache, v_cache, block_table,
+                                              max_blocks_per_seq, num_blocks, batch, n, n,
+                                              kv_heads, row_bytes, nullptr, (hipStream_t)stream),
+                      "prefix_export");
+}
+
 size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                 int32_t num_splits) {

@@ -94,6 +94,14 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
                             const void* k_new, const void* v_new, int32_t num_tokens,
                             const int64_t* slot_mapping, int64_t row_bytes, hipStream_t stream);
 
+// Prefix copies between a dense [batch, heads, src_len, D] cache and paged
+// slots; to_dense = export (then src_len == n and seqused_k is unused).
+hipError_t launch_prefix_copy(bool to_dense, void* dst_k, void* dst_v, const void* src_k,
+                              const void* src_v, const int32_t* block_table, int32_t max_blocks,
+                              int32_t num_blocks, int32_t batch, int32_t n, int32_t src_len,
+                              int32_t heads, int64_t row_bytes, int32_t* seqused_k,
+                              hipStream_t stream);
+
 // Vector-ALU path for units with one query row (q_len == 1) and group <= 8.
 // Returns hipErrorInvalidValue when no kernel is compiled for (dtype, D, group).
 hipError_t launch_attn_vec(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,

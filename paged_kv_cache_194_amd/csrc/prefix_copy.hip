@@ -1,0 +1,124 @@
+// Prefix import and export: raw copies between a dense prefill cache
+// [B, kv_heads, S, head_dim] and the slots of a paged cache
+// [num_blocks, 16, kv_heads, head_dim].
+//
+// vLLM-Omni paged_decode, PagedDecodeCache.load_prefix / _write_prefix: the
+// prefill K/V of a layer become one [kv_heads, head_dim] row per position and
+// the first n positions are copied into the cache slots (the tail keeps
+// whatever it held), then the live length is set to n; to_dynamic_cache copies
+// the first n slots back out as [1, kv_heads, n, head_dim] for the stage that
+// reads an ordinary cache.  Here every sequence of a batch is copied through
+// its own block-table row.
+//
+// Both directions are transposes of (head, position) with head_dim-long rows
+// contiguous on both sides, so no LDS staging is needed: a row is at least one
+// 16-byte chunk and, at the usual head_dim, one or more whole 128-byte lines.
+// Each work group owns one 16-position block of one sequence (one block-table
+// entry, read once by the group) and walks its chunks in the order of the
+// DESTINATION, so consecutive lanes store consecutive 16-byte chunks: the 16
+// slots of a pool block are one contiguous [16, H, D] span on import, and the
+// 16 rows of a head plane are one contiguous [16, D] span per head on export.
+#include "internal.h"
+#include "device_util.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kCopyThreads = 256;
+
+// grid: x = B * ceil(n / 16) (one 16-position block of one sequence),
+//       y = ceil(16 * H * C / 256) chunk groups of that block.
+template <bool EXPORT>
+__global__ __launch_bounds__(kCopyThreads) void prefix_copy_kernel(
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v,
+    const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
+    const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t num_blocks,
+    int32_t blocks_per_seq, int32_t n, int32_t src_len, int32_t heads, int32_t chunks_per_row,
+    int32_t* __restrict__ seqused_k, int32_t batch) {
+    const int32_t b = (int32_t)blockIdx.x / blocks_per_seq;
+    const int32_t blk = (int32_t)blockIdx.x - b * blocks_per_seq;
+    const int32_t idx = (int32_t)(blockIdx.y * kCopyThreads + threadIdx.x);
+    // set_length(n): the first block of each sequence also publishes its
+    // live length (one lane; the copy itself never reads it).
+    if (seqused_k && blk == 0 && blockIdx.y == 0 && threadIdx.x == 0) seqused_k[b] = n;
+
+    const int32_t row_chunks = heads * chunks_per_row;        // chunks of one slot row
+    if (idx >= 16 * row_chunks) return;
+    const int64_t row_bytes = (int64_t)chunks_per_row * 16;
+    const int32_t entry = block_table[(int64_t)b * max_blocks + blk];
+    const bool live = entry >= 0 && entry < num_blocks;
+
+    int32_t r, h, c;
+    if (EXPORT) {               // destination order: head, position, chunk
+        const int32_t plane = 16 * chunks_per_row;
+        h = idx / plane;
+        const int32_t rem = idx - h * plane;
+        r = rem / chunks_per_row;
+        c = rem - r * chunks_per_row;
+    } else {                    // destination order: position, head, chunk
+        r = idx / row_chunks;
+        const int32_t rem = idx - r * row_chunks;
+        h = rem / chunks_per_row;
+        c = rem - h * chunks_per_row;
+    }
+    const int32_t j = blk * 16 + r;
+    if (j >= n) return;
+    const int64_t slot_off = (((int64_t)entry * 16 + r) * heads + h) * row_bytes + (int64_t)c * 16;
+    if (EXPORT) {
+        const int64_t off = (((int64_t)b * heads + h) * n + j) * row_bytes + (int64_t)c * 16;
+        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (live) {
+            kv = ld16(src_k + slot_off);
+            vv = ld16(src_v + slot_off);
+        }
+        st16(dst_k + off, kv);
+        st16(dst_v + off, vv);
+    } else {
+        if (!live) return;
+        const int64_t off = (((int64_t)b * heads + h) * src_len + j) * row_bytes + (int64_t)c * 16;
+        const u32x4 kv = ld16(src_k + off);
+        const u32x4 vv = ld16(src_v + off);
+        st16(dst_k + slot_off, kv);
+        st16(dst_v + slot_off, vv);
+    }
+}
+
+// n == 0 with a length to publish: nothing to copy.
+__global__ __launch_bounds__(kCopyThreads) void set_length_kernel(int32_t* __restrict__ seqused_k,
+                                                                  int32_t batch, int32_t n) {
+    const int32_t i = (int32_t)(blockIdx.x * kCopyThreads + threadIdx.x);
+    if (i < batch) seqused_k[i] = n;
+}
+
+}  // namespace
+
+hipError_t launch_prefix_copy(bool to_dense, void* dst_k, void* dst_v, const void* src_k,
+                              const void* src_v, const int32_t* block_table, int32_t max_blocks,
+                              int32_t num_blocks, int32_t batch, int32_t n, int32_t src_len,
+                              int32_t heads, int64_t row_bytes, int32_t* seqused_k,
+                              hipStream_t stream) {
+    if (n == 0) {
+        if (!seqused_k) return hipSuccess;
+        set_length_kernel<<<dim3((uint32_t)((batch + kCopyThreads - 1) / kCopyThreads)),
+                            dim3(kCopyThreads), 0, stream>>>(seqused_k, batch, n);
+        return hipGetLastError();
+    }
+    const int32_t cpr = (int32_t)(row_bytes / 16);
+    const int32_t blocks_per_seq = (n + 15) / 16;
+    const dim3 grid((uint32_t)((int64_t)batch * blocks_per_seq),
+                    (uint32_t)(((int64_t)16 * heads * cpr + kCopyThreads - 1) / kCopyThreads));
+    if (to_dense)
+        prefix_copy_kernel<true><<<grid, dim3(kCopyThreads), 0, stream>>>(
+            (uint8_t*)dst_k, (uint8_t*)dst_v, (const uint8_t*)src_k, (const uint8_t*)src_v,
+            block_table, max_blocks, num_blocks, blocks_per_seq, n, src_len, heads, cpr, nullptr,
+            batch);
+    else
+        prefix_copy_kernel<false><<<grid, dim3(kCopyThreads), 0, stream>>>(
+            (uint8_t*)dst_k, (uint8_t*)dst_v, (const uint8_t*)src_k, (const uint8_t*)src_v,
+            block_table, max_blocks, num_blocks, blocks_per_seq, n, src_len, heads, cpr, seqused_k,
+            batch);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -7,6 +7,10 @@ for every length in the bucket; crossing a bucket edge reallocates (`grow`,
 built in locals and published in one step) and bumps `generation`, which keys
 the captures of DecodeGraphRunner.
 
+load_prefix / from_dynamic_cache bring a prefill cache in and
+to_dynamic_cache hands the decoded prefix back out, each layer one library
+copy (pkv.prefix_import / pkv.prefix_export).
+
 Here the whole step of a layer -- append this token's K/V at position
 length-1 and attend over the live prefix -- is one library call
 (pkv.paged_decode_attn with k_new/v_new): the write slot is derived on the
@@ -15,11 +19,11 @@ step changes.
 """
 from __future__ import annotations
 
-from typing import Callable, Dict, List, Optional, Tuple
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import BLOCK_SIZE, attn_workspace_bytes, paged_decode_attn
+from . import BLOCK_SIZE, attn_workspace_bytes, paged_decode_attn, prefix_export, prefix_import
 
 BUCKETS = (512, 1024, 2048, 4096, 8192)
 TAIL_STEP = 2048
@@ -99,6 +103,50 @@ class PagedDecodeCache:
         self.generation += 1
         self.set_length(n)
         return True
+
+    def load_prefix(self, keys: Sequence[Optional[torch.Tensor]],
+                    values: Sequence[Optional[torch.Tensor]]) -> bool:
+        """Copy a prefill cache (per layer ``[1, Hkv, S, D]``) into slots
+        ``[:S]`` and make S the live length; the tail keeps stale data.
+        Returns False when the prefill cache is empty."""
+        if not keys or keys[0] is None:
+            return False
+        if len(keys) != self.num_layers or len(values) != self.num_layers:
+            raise ValueError("one prefill K and V per layer expected")
+        prefix = keys[0].shape[2]
+        if prefix > self.bucket:
+            raise ValueError(f"prefix {prefix} exceeds bucket {self.bucket}; grow first")
+        for i in range(self.num_layers):
+            # The last layer's launch also publishes the live length.
+            prefix_import(self.k[i], self.v[i], keys[i], values[i], self.block_table, prefix,
+                          seqused_k=self.seqused if i == self.num_layers - 1 else None)
+        self._length = prefix
+        return True
+
+    @classmethod
+    def from_dynamic_cache(cls, keys, values, q_heads: int, device, dtype, min_length: int = 0,
+                           **kw) -> Optional["PagedDecodeCache"]:
+        """A cache whose bucket holds the prefill prefix plus the next token
+        (at least ``min_length``), loaded with that prefix; None if empty."""
+        if not keys or keys[0] is None:
+            return None
+        _, kv_heads, prefix, head_dim = keys[0].shape
+        obj = cls(len(keys), q_heads, kv_heads, head_dim, max(prefix + 1, min_length), device, dtype,
+                  **kw)
+        obj.load_prefix(keys, values)
+        return obj
+
+    def to_dynamic_cache(self) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+        """Per layer, slots ``[:length]`` copied out as contiguous
+        ``[1, Hkv, length, D]`` K and V (the hand-off to an ordinary cache)."""
+        n, H, D = self._length, self.kv_heads, self.head_dim
+        out = []
+        for i in range(self.num_layers):
+            k = torch.empty((1, H, n, D), device=self.device, dtype=self.dtype)
+            v = torch.empty((1, H, n, D), device=self.device, dtype=self.dtype)
+            prefix_export(k, v, self.k[i], self.v[i], self.block_table)
+            out.append((k, v))
+        return out
 
     def attend(self, layer: int, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                out: torch.Tensor) -> torch.Tensor:

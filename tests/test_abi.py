@@ -139,6 +139,46 @@ def test_kv_append_host_errors():
     assert L.pkv_kv_append(None, None, 16, None, None, -1, None, 2, 128, BF16, None) == EINVAL
 
 
+def _import(**over):
+    a = dict(kc=None, vc=None, nb=4, bs=16, ks=None, vs=None, B=1, S=20, n=18, bt=None, mb=2,
+             used=None, hkv=2, d=128, dtype=BF16)
+    a.update(over)
+    return pkv.lib().pkv_prefix_import(a["kc"], a["vc"], a["nb"], a["bs"], a["ks"], a["vs"], a["B"],
+                                       a["S"], a["n"], a["bt"], a["mb"], a["used"], a["hkv"], a["d"],
+                                       a["dtype"], None)
+
+
+def _export(**over):
+    a = dict(kd=None, vd=None, kc=None, vc=None, nb=4, bs=16, B=1, n=18, bt=None, mb=2, hkv=2,
+             d=128, dtype=BF16)
+    a.update(over)
+    return pkv.lib().pkv_prefix_export(a["kd"], a["vd"], a["kc"], a["vc"], a["nb"], a["bs"], a["B"],
+                                       a["n"], a["bt"], a["mb"], a["hkv"], a["d"], a["dtype"], None)
+
+
+def test_prefix_copy_host_errors():
+    p, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4104)
+    full = dict(kc=p, vc=p, ks=p, vs=p, bt=p)
+    assert _import() == EINVAL                                   # null pointers with n > 0
+    assert _import(n=0) == 0                                     # nothing to copy or publish
+    assert _import(B=0, **full) == 0
+    assert _import(S=10, **full) == EINVAL                       # n > src_len
+    assert _import(n=33, S=40, **full) == EINVAL                 # n > 16 * max_blocks
+    assert _import(bs=8, **full) == EINVAL
+    assert _import(d=12, **full) == EINVAL
+    assert _import(nb=0, **full) == EINVAL
+    assert _import(n=-1, **full) == EINVAL
+    assert _import(dtype=7, **full) == EINVAL
+    assert _import(**{**full, "ks": odd}) == EINVAL             # misaligned source
+    fe = dict(kd=p, vd=p, kc=p, vc=p, bt=p)
+    assert _export() == EINVAL
+    assert _export(n=0) == 0
+    assert _export(B=0, **fe) == 0
+    assert _export(n=33, **fe) == EINVAL
+    assert _export(**{**fe, "vd": odd}) == EINVAL
+    assert _export(B=1 << 23, n=32, mb=2, **fe) == EINVAL        # 2^24 work groups: too many
+
+
 def test_split_choice_is_static_and_bounded():
     # depends only on host arguments; more units -> fewer splits
     a = pkv.attn_num_splits(1, 1, 4096, 32, 8, 128, 0)

@@ -201,6 +201,41 @@ def paged_inputs(*, seed: int, lengths, q_lens, q_heads: int, kv_heads: int,
         name=name)
 
 
+@dataclass
+class PrefixInputs:
+    """A dense prefill cache ``[B, Hkv, S, D]`` and a paged pool to copy it into.
+
+    ``block_table`` deals each sequence the blocks of its first ``n`` positions
+    from a random permutation of the pool (or in order with ``identity``);
+    pool blocks no sequence owns hold NaN.  ``bad_entries`` lists
+    ``(sequence, table column, value)`` entries overwritten with ids outside the
+    pool.
+    """
+    k_src: torch.Tensor
+    v_src: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    n: int
+
+
+def prefix_inputs(*, seed: int, batch: int, kv_heads: int, head_dim: int, src_len: int, n: int,
+                  num_blocks: int, max_blocks: int, dtype, device="cpu", identity: bool = False,
+                  bad_entries=()) -> PrefixInputs:
+    table, used = deal_block_tables([n] * batch, num_blocks, max_blocks, seed + 1, identity)
+    for b, col, val in bad_entries:
+        table[b, col] = int(val)
+    k_src = randn((batch, kv_heads, src_len, head_dim), dtype, seed + 2, device)
+    v_src = randn((batch, kv_heads, src_len, head_dim), dtype, seed + 3, device)
+    k_cache = randn((num_blocks, BLOCK, kv_heads, head_dim), dtype, seed + 4, device)
+    v_cache = randn((num_blocks, BLOCK, kv_heads, head_dim), dtype, seed + 5, device)
+    unused = (~used).to(device)
+    k_cache[unused] = float("nan")
+    v_cache[unused] = float("nan")
+    return PrefixInputs(k_src=k_src, v_src=v_src, k_cache=k_cache, v_cache=v_cache,
+                        block_table=table.to(device), n=int(n))
+
+
 def column_inputs(*, seed: int, rows: int, cols: int, q_lens, kv_ends, total_q: int,
                   q_heads: int, kv_heads: int, head_dim: int, dtype, causal: bool,
                   window: int, scale: Optional[float] = None, device="cpu",
