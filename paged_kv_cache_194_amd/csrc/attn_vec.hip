@@ -328,10 +328,10 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             const int tt = j * KTPW + ktok;
             const int64_t a = tok_addr(blk, id, tt);
 #pragma unroll
-            for (int c = 0; c < KCH; ++c) kr[j][c] = ld16(Kb + a + (kpart + KLPT * c) * 16);
+            for (int c = 0; c < KCH; ++c) kr[j][c] = ld16_stream(Kb + a + (kpart + KLPT * c) * 16);
         }
 #pragma unroll
-        for (int j = 0; j < VNI; ++j) vr[j] = ld16(Vb + tok_addr(blk, id, j * VTPW + vtok) + vpart * 16);
+        for (int j = 0; j < VNI; ++j) vr[j] = ld16_stream(Vb + tok_addr(blk, id, j * VTPW + vtok) + vpart * 16);
         if (fuse && blk == (pn >> 4)) {         // this step's token: from k_new, and stored
             uint8_t* Kw = (uint8_t*)p.k;
             uint8_t* Vw = (uint8_t*)p.v;

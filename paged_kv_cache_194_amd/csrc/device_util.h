@@ -17,6 +17,13 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Nontemporal 16-byte load: for bytes a kernel reads exactly once.
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    const u32v4 v = __builtin_nontemporal_load(reinterpret_cast<const u32v4*>(p));
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+
 __device__ __forceinline__ void st16(void* p, const u32x4& v) {
     *reinterpret_cast<u32x4*>(p) = v;
 }
