@@ -341,6 +341,22 @@ def bench_prefix(args, torch):
 
     layer_bytes = 2 * n * m.kv_heads * m.head_dim * 2          # K + V of one layer
     step_bytes = 4 * m.layers * layer_bytes                      # import r+w, export r+w
+    if args.eager:
+        # plain launches (hardware counters are taken per dispatch)
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.steps):
+            step()
+        e.record()
+        torch.cuda.synchronize()
+        res = {"metric": "prefill hand-over copy GB/s (import + export)",
+               "eager_us_per_step": round(s.elapsed_time(e) * 1e3 / args.steps, 2)}
+        if args.copy_ceiling:
+            res["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
+        return res
     g = capture(torch, step)
     time_graph(torch, g, max(1, args.warmup))
     t_wall0 = time.perf_counter()
@@ -492,7 +508,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ceiling", action="store_true", help="also time a 4 GiB device copy")
     ap.add_argument("--eager", action="store_true",
-                    help="c2 only: plain launches instead of graph replays (for per-dispatch counters)")
+                    help="c2 and prefix: plain launches instead of graph replays (for per-dispatch counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
