@@ -30,6 +30,10 @@ support in the design notes):
 * causal alignment is bottom-right: row i of a unit with L rows and E keys
   sits at position ``p = E - L + i``;
 * a window W shows keys ``p - W + 1 .. p`` (W keys including the query);
+* a left-padding bound ``kv_start > 0`` (per sequence or segment) hides the
+  keys before it; a row at a position before it sees only its own key (the
+  diagonal the pages always keep), also without ``causal``; ``kv_start <= 0``
+  is no padding;
 * GQA: q head h reads kv head ``h // (Hq // Hkv)``;
 * a row with no visible key, and a row no unit covers, is 0;
 * paged ``seqused_k`` is clamped to ``[0, min(max_seqlen_k, 16*max_blocks)]``;
@@ -140,12 +144,23 @@ def gather_slots_paged(block_table_row, E: int, num_blocks: int):
 # --------------------------------------------------------------------------
 
 
-def visible_range(E: int, L: int, i: int, causal: bool, window: int) -> tuple[int, int]:
+def visible_range(E: int, L: int, i: int, causal: bool, window: int,
+                  kv_start: int = 0) -> tuple[int, int]:
     """Half-open key range ``[lo, hi)`` that row ``i`` of ``L`` new queries sees
-    over ``E`` keys.  The row sits at position ``p = E - L + i``."""
+    over ``E`` keys.  The row sits at position ``p = E - L + i``.
+
+    ``kv_start > 0`` is a left-padding bound (tiny-llm ``kv_cache.py``,
+    ``padded_causal_mask`` and the module docstring): keys before it are
+    hidden, and a query before it (a pad query) still sees its own key, so no
+    row is left without keys.
+    """
     p = E - L + i
+    if kv_start > 0 and p < kv_start:
+        lo, hi = max(p, 0), min(p + 1, E)
+        return lo, max(lo, hi)
     hi = min(E, p + 1) if causal else E
     lo = max(0, p - window + 1) if window > 0 else 0
+    lo = max(lo, kv_start)
     return lo, max(lo, hi)
 
 
@@ -156,13 +171,14 @@ def visible_range(E: int, L: int, i: int, causal: bool, window: int) -> tuple[in
 
 def attend_unit(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, key_ok: np.ndarray,
                 E: int, scale: float, causal: bool, window: int,
-                chunk: int = 64) -> np.ndarray:
+                chunk: int = 64, kv_start: int = 0) -> np.ndarray:
     """softmax(q K^T * scale) V for the ``L`` query rows of one unit.
 
     q      float64 [L, Hq, D]
     keys   float64 [E, Hkv, D]  logical keys 0..E-1 (entries outside ``key_ok`` unused)
     vals   float64 [E, Hkv, D]
     key_ok bool [E]  keys that have storage (see the block-id rule above)
+    kv_start  left-padding bound of the unit (see ``visible_range``)
     Returns float64 [L, Hq, D]; a row with no visible key is 0.
 
     Rows are taken ``chunk`` at a time over the union of their key ranges with
@@ -177,7 +193,7 @@ def attend_unit(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, key_ok: np.nd
     if L == 0 or E <= 0:
         return out
     key_ok = np.asarray(key_ok, dtype=bool)
-    ranges = [visible_range(E, L, i, causal, window) for i in range(L)]
+    ranges = [visible_range(E, L, i, causal, window, kv_start) for i in range(L)]
     with np.errstate(invalid="ignore", over="ignore"):
         _attend_chunks(q, keys, vals, key_ok, ranges, scale, G, Hkv, D, L, chunk, out)
     return out
@@ -234,14 +250,15 @@ def _attend_chunks(q, keys, vals, key_ok, ranges, scale, G, Hkv, D, L, chunk, ou
 def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *,
                     dtype: str, scale: float, causal: bool = False, window: int = 0,
                     max_seqlen_q: int | None = None, max_seqlen_k: int | None = None,
-                    seqs=None) -> np.ndarray:
+                    seqs=None, kv_start=None) -> np.ndarray:
     """Oracle for varlen attention over a paged cache.
 
     q        raw [total_q, Hq, D]          (bits for bf16, float32 for f32)
     k_cache  raw [num_blocks, 16, Hkv, D]  (or any view with a flat slot axis)
     block_table int [num_seqs, max_blocks]; cu_seqlens_q int [num_seqs+1];
     seqused_k int [num_seqs].  ``seqs`` restricts the work to some sequences
-    (the other rows are left 0, as uncovered rows are).
+    (the other rows are left 0, as uncovered rows are).  ``kv_start`` int
+    [num_seqs] or None: each sequence's left-padding bound.
     Returns float64 [total_q, Hq, D].
     """
     q = np.asarray(q)
@@ -270,7 +287,8 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *
         keys = to_f64(k_flat[slots], dtype)
         vals = to_f64(v_flat[slots], dtype)
         qq = to_f64(q[start:stop], dtype)
-        res = attend_unit(qq, keys, vals, ok, E, scale, causal, window)
+        ks = 0 if kv_start is None else int(kv_start[b])
+        res = attend_unit(qq, keys, vals, ok, E, scale, causal, window, kv_start=ks)
         for i in range(n_rows):
             r = start + i
             if 0 <= r < total_q:
@@ -285,10 +303,11 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *
 
 def column_attention(q, k_store, v_store, seq_info, *, dtype: str, scale: float,
                      causal: bool, window: int, max_seqlen_q: int | None = None,
-                     segments=None) -> np.ndarray:
+                     segments=None, kv_start=None) -> np.ndarray:
     """Oracle for ``sdpa_varlen`` over a column (ring) store.  Key ``j`` of the
-    segment's column sits in store row ``j % rows``.  Returns float64
-    [total_q, Hq, D] with uncovered rows 0."""
+    segment's column sits in store row ``j % rows``.  ``kv_start`` int
+    [num_segments] or None: each segment's left-padding bound.  Returns
+    float64 [total_q, Hq, D] with uncovered rows 0."""
     q = np.asarray(q)
     total_q, Hq, D = q.shape
     ks = np.asarray(k_store)
@@ -301,12 +320,13 @@ def column_attention(q, k_store, v_store, seq_info, *, dtype: str, scale: float,
         if L <= 0:
             continue
         E = max(E, 0)
+        pad = 0 if kv_start is None else int(kv_start[s])
         n_rows = L if max_seqlen_q is None else min(L, int(max_seqlen_q))
         # Only the keys some row can see are gathered (the rest may be
         # overwritten ring rows); unseen keys are zero placeholders.
         lo_all = E
         for i in range(n_rows):
-            lo, hi = visible_range(E, L, i, causal, window)
+            lo, hi = visible_range(E, L, i, causal, window, pad)
             if hi > lo:
                 lo_all = min(lo_all, lo)
         keys = np.zeros((E, ks.shape[2], D), dtype=np.float64)
@@ -321,7 +341,7 @@ def column_attention(q, k_store, v_store, seq_info, *, dtype: str, scale: float,
         lo_r, hi_r = max(q_start, 0), min(q_start + L, total_q)
         if hi_r > lo_r:
             qq[lo_r - q_start:hi_r - q_start] = to_f64(q[lo_r:hi_r], dtype)
-        res = attend_unit(qq, keys, vals, ok, E, scale, causal, window)
+        res = attend_unit(qq, keys, vals, ok, E, scale, causal, window, kv_start=pad)
         for i in range(n_rows):
             r = q_start + i
             if 0 <= r < total_q:

@@ -564,6 +564,62 @@ def pin_prefix_roundtrip_permuted():
     assert changed.tolist() == expect
 
 
+def pin_golden_padded_mask():
+    """The pages' left-padded causal rule, worked by hand, as key ranges; and
+    through the paged oracle: a pad row's output is its own value row exactly."""
+    fx = _load("padded_mask.json")
+    for c in fx["cases"]:
+        E, L, fv = c["start"] + c["T"], c["T"], c["first_valid"]
+        for i, want in enumerate(c["visible"]):
+            lo, hi = oracle.visible_range(E, L, i, True, 0, fv)
+            assert list(range(lo, hi)) == want, (c, i)
+    rng = np.random.default_rng(41)
+    E, L, fv, D = 8, 4, 7, 8                     # rows at 4, 5, 6 are pad rows
+    k = rng.standard_normal((16, 1, 1, D)).astype(np.float32)
+    v = rng.standard_normal((16, 1, 1, D)).astype(np.float32)
+    q = rng.standard_normal((L, 1, D)).astype(np.float32)
+    out = oracle.paged_attention(q, k, v, np.array([[0]]), np.array([0, L]), np.array([E]),
+                                 dtype="f32", scale=0.3, causal=True, kv_start=np.array([fv]))
+    for i in range(3):
+        assert np.array_equal(out[i, 0], v[4 + i, 0, 0].astype(np.float64))
+
+
+def pin_left_padding_is_translation():
+    """Valid rows over a left-padded prefix equal the same rows over the
+    prefix with the pad keys cut off (no padding), causal and non-causal, with
+    a window, through a permuted table; kv_start <= 0 is no padding."""
+    rng = np.random.default_rng(42)
+    Hq, Hkv, D, E, L, pad = 4, 2, 16, 45, 5, 13
+    q = rng.standard_normal((L, Hq, D)).astype(np.float32)
+    keys = rng.standard_normal((E, Hkv, D)).astype(np.float32)
+    vals = rng.standard_normal((E, Hkv, D)).astype(np.float32)
+
+    def paged(kk, vv, n, seed):
+        nb = (n + 15) // 16 + 2
+        perm = np.random.default_rng(seed).permutation(nb)
+        kc = np.full((nb * 16, Hkv, D), np.nan, np.float32)
+        vc = np.full((nb * 16, Hkv, D), np.nan, np.float32)
+        for j in range(n):
+            kc[perm[j // 16] * 16 + j % 16] = kk[j]
+            vc[perm[j // 16] * 16 + j % 16] = vv[j]
+        return kc, vc, perm[None, :]
+
+    kc, vc, bt = paged(keys, vals, E, 1)
+    kt, vt, btt = paged(keys[pad:], vals[pad:], E - pad, 2)
+    for causal, window in ((True, 0), (False, 0), (True, 30), (False, 30)):
+        a = oracle.paged_attention(q, kc, vc, bt, np.array([0, L]), np.array([E]), dtype="f32",
+                                   scale=0.25, causal=causal, window=window, kv_start=np.array([pad]))
+        b = oracle.paged_attention(q, kt, vt, btt, np.array([0, L]), np.array([E - pad]), dtype="f32",
+                                   scale=0.25, causal=causal, window=window)
+        assert np.allclose(a, b, rtol=0, atol=1e-12), (causal, window)
+        none = oracle.paged_attention(q, kc, vc, bt, np.array([0, L]), np.array([E]), dtype="f32",
+                                      scale=0.25, causal=causal, window=window)
+        for ks in (0, -3):
+            z = oracle.paged_attention(q, kc, vc, bt, np.array([0, L]), np.array([E]), dtype="f32",
+                                       scale=0.25, causal=causal, window=window, kv_start=np.array([ks]))
+            assert np.array_equal(z, none)
+
+
 ALL_PINS = [
     pin_bf16_decode,
     pin_golden_causal_rule, pin_golden_slots, pin_golden_closed_forms, pin_window_span,
@@ -572,6 +628,7 @@ ALL_PINS = [
     pin_uncovered_rows_zero, pin_window_large_is_none, pin_ring_equals_unrolled, pin_gqa_repeat,
     pin_closed_form_means, pin_kv_append_bits,
     pin_golden_prefix_copy, pin_prefix_identity_is_transpose, pin_prefix_roundtrip_permuted,
+    pin_golden_padded_mask, pin_left_padding_is_translation,
 ]
 
 
@@ -584,21 +641,21 @@ def test_oracle_pin(pin):
 # Planted mistakes: each must make at least one pin fail.
 # ---------------------------------------------------------------------------
 
-def _top_left_causal(E, L, i, causal, window):
+def _top_left_causal(E, L, i, causal, window, kv_start=0):
     p = i
     hi = min(E, p + 1) if causal else E
     lo = max(0, p - window + 1) if window > 0 else 0
     return lo, max(lo, hi)
 
 
-def _window_off_by_one(E, L, i, causal, window):
+def _window_off_by_one(E, L, i, causal, window, kv_start=0):
     p = E - L + i
     hi = min(E, p + 1) if causal else E
     lo = max(0, p - window) if window > 0 else 0
     return lo, max(lo, hi)
 
 
-def _causal_excludes_self(E, L, i, causal, window):
+def _causal_excludes_self(E, L, i, causal, window, kv_start=0):
     p = E - L + i
     hi = min(E, p) if causal else E
     lo = max(0, p - window + 1) if window > 0 else 0
@@ -623,16 +680,16 @@ def _gather_no_table(row, E, nb):
 _real_attend = oracle.attend_unit
 
 
-def _attend_no_scale(q, keys, vals, ok, E, scale, causal, window, chunk=64):
-    return _real_attend(q, keys, vals, ok, E, 1.0, causal, window, chunk)
+def _attend_no_scale(q, keys, vals, ok, E, scale, causal, window, chunk=64, kv_start=0):
+    return _real_attend(q, keys, vals, ok, E, 1.0, causal, window, chunk, kv_start)
 
 
-def _attend_swapped_kv(q, keys, vals, ok, E, scale, causal, window, chunk=64):
-    return _real_attend(q, vals, keys, ok, E, scale, causal, window, chunk)
+def _attend_swapped_kv(q, keys, vals, ok, E, scale, causal, window, chunk=64, kv_start=0):
+    return _real_attend(q, vals, keys, ok, E, scale, causal, window, chunk, kv_start)
 
 
-def _attend_last_kv_head(q, keys, vals, ok, E, scale, causal, window, chunk=64):
-    return _real_attend(q, keys[:, ::-1], vals[:, ::-1], ok, E, scale, causal, window, chunk)
+def _attend_last_kv_head(q, keys, vals, ok, E, scale, causal, window, chunk=64, kv_start=0):
+    return _real_attend(q, keys[:, ::-1], vals[:, ::-1], ok, E, scale, causal, window, chunk, kv_start)
 
 
 _real_ring = oracle.ring_slot
@@ -665,6 +722,23 @@ def _export_shifted(kf, vf, bt, B, n):
     return ke[:, :, 1:], ve[:, :, 1:]
 
 
+_real_visible = oracle.visible_range
+
+
+def _padding_ignored(E, L, i, causal, window, kv_start=0):
+    return _real_visible(E, L, i, causal, window, 0)
+
+
+def _pad_rows_see_nothing(E, L, i, causal, window, kv_start=0):
+    if kv_start > 0 and E - L + i < kv_start:
+        return 0, 0
+    return _real_visible(E, L, i, causal, window, kv_start)
+
+
+def _padding_off_by_one(E, L, i, causal, window, kv_start=0):
+    return _real_visible(E, L, i, causal, window, kv_start + 1 if kv_start > 0 else 0)
+
+
 MUTANTS = [
     ("visible_range", _top_left_causal),
     ("visible_range", _window_off_by_one),
@@ -683,6 +757,9 @@ MUTANTS = [
     ("prefix_import", _import_s_h_mixed),
     ("prefix_export", _export_shifted),
     ("paged_slot", lambda row, j: int(row[j // 16]) * 16 + 15 - j % 16),
+    ("visible_range", _padding_ignored),
+    ("visible_range", _pad_rows_see_nothing),
+    ("visible_range", _padding_off_by_one),
 ]
 
 
