@@ -19,7 +19,8 @@
  *    covers zeroed, split-K for short steps; in-graph writes to slot
  *    (position % rows) * columns + column.
  *  - tiny-llm kv_cache.py, causal_kwargs: with T new queries over start + T
- *    keys, query i sees keys 0 .. start + i.
+ *    keys, query i sees keys 0 .. start + i; padded_causal_mask: keys before a
+ *    row's first valid position are hidden, the diagonal always kept.
  *
  * Conventions for every call:
  *  - All pointers are DEVICE pointers unless stated.  The caller owns every
@@ -41,7 +42,8 @@
  *      E = clamp(seqused_k[b], 0, min(max_seqlen_k, 16 * max_blocks_per_seq));
  *      column-mode kv_end below 0 counts as 0;
  *      row i of a unit with L query rows sits at position p = E - L + i and
- *      sees keys j with j < E, (causal: j <= p), (window > 0: j >= p - window + 1);
+ *      sees keys j with j < E, (causal: j <= p), (window > 0: j >= p - window + 1),
+ *      (kv_start[u] = s > 0: j >= s, and a row with p < s sees only key p);
  *      a live key whose block-table entry is outside [0, num_blocks), or a
  *      segment whose column is outside [0, cols), contributes no keys;
  *      a row with no visible key is 0, and so is every row of [0, total_q)
@@ -114,6 +116,12 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  * softmax_scale: multiplies q.k before the softmax.
  * causal       : with one query per sequence causal equals non-causal.
  * window       : > 0 keeps the last `window` keys (p - window + 1 .. p).
+ * kv_start     : optional int32 [num_seqs] left-padding bound (tiny-llm kv_cache.py,
+ *                padded_causal_mask: first_valid per row): keys before
+ *                kv_start[b] are hidden, and a query at a position before it (a
+ *                pad query) sees only its own key.  NULL, or an entry <= 0, is no
+ *                padding.  Keys below the bound never reach the output (NaN
+ *                included), and whole 16-key blocks below it are not read.
  * num_splits   : split-K partitions per (sequence, kv head) on average; 0 lets the
  *                library pick from the host arguments.  With one sequence the
  *                live keys are cut into num_splits ranges; with several, the
@@ -138,8 +146,8 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q,
                                  const void* k_new, const void* v_new,
                                  int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                  float softmax_scale, int32_t causal, int32_t window,
-                                 int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                 pkv_dtype dtype, void* stream);
+                                 const int32_t* kv_start, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, pkv_dtype dtype, void* stream);
 
 /*
  * pkv_varlen_attn -- packed query rows over a paged cache or a column store.
@@ -161,6 +169,10 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q,
  * max_seqlen_k : host bound on the keys a unit sees.  Paged mode clamps
  *                seqused_k to it.  Column mode uses it only to choose the split
  *                count and requires it > 0 (e.g. window + max_seqlen_q - 1, or rows).
+ * kv_start     : optional int32 [num_seqs] (paged) or [num_segments] (column):
+ *                the left-padding bound of each unit, as for pkv_paged_decode_attn;
+ *                with several query rows each row before the bound (a pad query)
+ *                sees only its own key, causal or not.
  * Other arguments as for pkv_paged_decode_attn.  workspace must hold
  * pkv_attn_workspace_bytes(units, max_seqlen_q, ...) bytes with units =
  * num_seqs or num_segments.
@@ -174,8 +186,8 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q,
                            int32_t max_seqlen_q, int32_t max_seqlen_k,
                            int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                            float softmax_scale, int32_t causal, int32_t window,
-                           int32_t num_splits, void* workspace, size_t workspace_bytes,
-                           pkv_dtype dtype, void* stream);
+                           const int32_t* kv_start, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, pkv_dtype dtype, void* stream);
 
 /*
  * pkv_prefix_import -- copy the first n positions of a dense prefill cache into

@@ -53,11 +53,11 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 _SIGS = {
     "pkv_kv_append": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _vp]),
     "pkv_paged_decode_attn": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
-                                     _vp, _vp, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz,
-                                     _i32, _vp]),
+                                     _vp, _vp, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _i32, _vp,
+                                     _sz, _i32, _vp]),
     "pkv_varlen_attn": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
-                               _i32, _i32, _vp, _sz, _i32, _vp]),
+                               _i32, _vp, _i32, _vp, _sz, _i32, _vp]),
     "pkv_prefix_import": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
                                  _i32, _i32, _i32, _vp]),
     "pkv_prefix_export": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32,
@@ -214,11 +214,12 @@ def paged_decode_attn(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                       causal: bool = False, window: int = 0, num_splits: int = 0,
                       workspace: Optional[torch.Tensor] = None,
                       k_new: Optional[torch.Tensor] = None,
-                      v_new: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      v_new: Optional[torch.Tensor] = None,
+                      kv_start: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One query per sequence: ``q``/``out`` ``[B, Hq, D]`` over ``[NB, 16, Hkv, D]`` caches.
     With ``k_new``/``v_new`` ``[B, Hkv, D]`` the token is appended at position
-    ``seqused_k[b] - 1`` first."""
-    _dev(out, q, k_cache, v_cache, block_table, seqused_k, k_new, v_new)
+    ``seqused_k[b] - 1`` first.  ``kv_start`` int32 ``[B]``: left-padding bounds."""
+    _dev(out, q, k_cache, v_cache, block_table, seqused_k, k_new, v_new, kv_start)
     _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, Hq, D]")
     _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "caches must be [NB, 16, Hkv, D]")
     _need(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [B, W]")
@@ -231,14 +232,16 @@ def paged_decode_attn(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
         _need(k_new is not None and v_new is not None, "give both k_new and v_new")
         _need(tuple(k_new.shape) == (B, Hkv, D) and k_new.shape == v_new.shape, "k_new/v_new must be [B, Hkv, D]")
         _need(k_new.dtype == v_new.dtype == q.dtype, "dtypes differ")
+    if kv_start is not None:
+        _need(kv_start.dtype == torch.int32 and kv_start.numel() == B, "kv_start must be int32 [B]")
     scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
     need = attn_workspace_bytes(B, 1, max_seqlen_k, Hq, Hkv, D, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q)
     _check(lib().pkv_paged_decode_attn(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), NB, BS, _ptr(block_table),
         block_table.shape[1], _ptr(seqused_k), B, int(max_seqlen_k), _ptr(k_new), _ptr(v_new),
-        Hq, Hkv, D, scale, int(bool(causal)), int(window), int(num_splits), _ptr(workspace),
-        ws_bytes, _dtype(q), _stream(q)))
+        Hq, Hkv, D, scale, int(bool(causal)), int(window), _ptr(kv_start), int(num_splits),
+        _ptr(workspace), ws_bytes, _dtype(q), _stream(q)))
     return out
 
 
@@ -249,11 +252,13 @@ def varlen_attn(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                 block_table: Optional[torch.Tensor] = None,
                 seq_info: Optional[torch.Tensor] = None,
                 softmax_scale: Optional[float] = None, causal: bool = False, window: int = 0,
-                num_splits: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                kv_start: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Packed rows ``q``/``out`` ``[total_q, Hq, D]`` over a paged cache
     (``cu_seqlens_q``, ``seqused_k``, ``block_table``; ``k``/``v`` ``[NB, 16, Hkv, D]``)
-    or a column store (``seq_info`` ``[S, 4]``; ``k``/``v`` ``[rows, cols, Hkv, D]``)."""
-    _dev(out, q, k, v, cu_seqlens_q, seqused_k, block_table, seq_info)
+    or a column store (``seq_info`` ``[S, 4]``; ``k``/``v`` ``[rows, cols, Hkv, D]``).
+    ``kv_start`` int32, one per sequence or segment: left-padding bounds."""
+    _dev(out, q, k, v, cu_seqlens_q, seqused_k, block_table, seq_info, kv_start)
     _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [total_q, Hq, D]")
     _need(k.dim() == 4 and k.shape == v.shape, "k/v must be 4-d and equal in shape")
     _need(q.dtype == k.dtype == v.dtype == out.dtype, "dtypes differ")
@@ -279,11 +284,14 @@ def varlen_attn(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Te
         num_segments = seq_info.shape[0]
         rows, cols = k.shape[0], k.shape[1]
         units = num_segments
+    if kv_start is not None:
+        _need(kv_start.dtype == torch.int32 and kv_start.numel() == units,
+              "kv_start must be int32, one per sequence or segment")
     need = attn_workspace_bytes(units, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q)
     _check(lib().pkv_varlen_attn(
         _ptr(out), _ptr(q), total_q, _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(seqused_k),
         num_seqs, _ptr(block_table), mb, nb, bs, _ptr(seq_info), num_segments, rows, cols,
         int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, scale, int(bool(causal)), int(window),
-        int(num_splits), _ptr(workspace), ws_bytes, _dtype(q), _stream(q)))
+        _ptr(kv_start), int(num_splits), _ptr(workspace), ws_bytes, _dtype(q), _stream(q)))
     return out

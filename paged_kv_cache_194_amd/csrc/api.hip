@@ -286,8 +286,9 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, 
                                  int32_t num_seqs, int32_t max_seqlen_k, const void* k_new,
                                  const void* v_new, int32_t q_heads, int32_t kv_heads,
                                  int32_t head_dim, float softmax_scale, int32_t causal,
-                                 int32_t window, int32_t num_splits, void* workspace,
-                                 size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+                                 int32_t window, const int32_t* kv_start, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                 void* stream) {
     pkv_status s = check_heads(q_heads, kv_heads, head_dim, dtype);
     if (s != PKV_OK) return s;
     if (block_size != PKV_BLOCK_SIZE) return fail(PKV_EINVAL, "block_size %d: must be 16", block_size);
@@ -321,6 +322,7 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, 
     p.v = v_cache;
     p.seqused_k = seqused_k;
     p.block_table = block_table;
+    p.kv_start = kv_start;
     p.mode = pkv::kPagedDecode;
     p.total_q = num_seqs;
     p.num_units = num_seqs;
@@ -344,8 +346,8 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q, const void
                            int32_t num_segments, int32_t rows, int32_t cols, int32_t max_seqlen_q,
                            int32_t max_seqlen_k, int32_t q_heads, int32_t kv_heads,
                            int32_t head_dim, float softmax_scale, int32_t causal, int32_t window,
-                           int32_t num_splits, void* workspace, size_t workspace_bytes,
-                           pkv_dtype dtype, void* stream) {
+                           const int32_t* kv_start, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, pkv_dtype dtype, void* stream) {
     pkv_status s = check_heads(q_heads, kv_heads, head_dim, dtype);
     if (s != PKV_OK) return s;
     const bool paged = block_table != nullptr;
@@ -398,6 +400,7 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q, const void
     p.group = group;
     p.causal = causal != 0;
     p.window = w;
+    p.kv_start = kv_start;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
     if (paged) {
         p.mode = pkv::kPagedVarlen;

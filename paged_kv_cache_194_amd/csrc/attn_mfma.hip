@@ -131,27 +131,37 @@ struct MfmaCfg {
 // Keys one row tile of a unit needs: the union of its rows' visible ranges,
 // from a 16-aligned start, in chunks of `bn` keys.  Row i of a unit of L rows
 // over E keys sits at position E - L + i (causal: keys up to it; window W:
-// the W keys ending there).
+// the W keys ending there; left-padding bound `pad` > 0: no key before it,
+// and a row before it keeps only its own key).  Both bounds are
+// non-decreasing in i, so a tile's union runs from its first row's lower
+// bound to its last row's upper bound.
 struct TileKeys {
     int32_t key_lo, key_hi, c_base, nchunk;
 };
-__device__ __forceinline__ int32_t row_lo(const AttnParams& p, int32_t E, int32_t L, int32_t i) {
-    if (p.window <= 0) return 0;
-    const int32_t lo = E - L + i - p.window + 1;
-    return lo > 0 ? lo : 0;
+__device__ __forceinline__ int32_t row_lo(const AttnParams& p, int32_t E, int32_t L, int32_t i,
+                                          int32_t pad) {
+    const int32_t pos = E - L + i;
+    if (pad > 0 && pos < pad) return pos > 0 ? pos : 0;
+    int32_t lo = 0;
+    if (p.window > 0) {
+        lo = pos - p.window + 1;
+        lo = lo > 0 ? lo : 0;
+    }
+    return lo > pad ? lo : (pad > 0 ? pad : lo);
 }
-__device__ __forceinline__ int32_t row_hi(const AttnParams& p, int32_t E, int32_t L, int32_t i) {
-    if (!p.causal) return E;
+__device__ __forceinline__ int32_t row_hi(const AttnParams& p, int32_t E, int32_t L, int32_t i,
+                                          int32_t pad) {
     const int32_t pos1 = E - L + i + 1;
-    return pos1 < E ? (pos1 > 0 ? pos1 : 0) : E;
+    if ((pad > 0 && pos1 <= pad) || p.causal) return pos1 < E ? (pos1 > 0 ? pos1 : 0) : E;
+    return E;
 }
 __device__ __forceinline__ TileKeys tile_keys(const AttnParams& p, int32_t E, int32_t L, int32_t M,
-                                              int32_t m0, int32_t bm, int32_t bn) {
+                                              int32_t m0, int32_t bm, int32_t bn, int32_t pad) {
     const int32_t G = p.group;
     const int32_t m_last = min(M, m0 + bm) - 1;
     TileKeys t;
-    t.key_lo = row_lo(p, E, L, m0 / G);
-    t.key_hi = max(row_hi(p, E, L, m_last / G), t.key_lo);
+    t.key_lo = row_lo(p, E, L, m0 / G, pad);
+    t.key_hi = max(row_hi(p, E, L, m_last / G, pad), t.key_lo);
     t.c_base = (t.key_lo >> 4) << 4;
     t.nchunk = t.key_hi > t.c_base ? (t.key_hi - t.c_base + bn - 1) / bn : 0;
     return t;
@@ -165,7 +175,7 @@ __device__ __forceinline__ int32_t mfma_item_chunks(const AttnParams& p, int32_t
     if (L <= 0 || (L == 1 && p.group <= 8)) return -1;
     const int32_t M = (L < p.max_seqlen_q ? L : p.max_seqlen_q) * p.group;
     if (tile * bm >= M) return -1;
-    return tile_keys(p, ui.keys_ok ? ui.kv_end : 0, L, M, tile * bm, bm, bn).nchunk;
+    return tile_keys(p, ui.keys_ok ? ui.kv_end : 0, L, M, tile * bm, bm, bn, ui.pad).nchunk;
 }
 
 template <int D, int NW, int RT, int BN, int NS, int WPE, bool PAGED>
@@ -245,10 +255,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     const int32_t Hkv = p.kv_heads;
 
     // The union of this tile's rows' visible ranges, cut into S parts.
-    const TileKeys tk = tile_keys(p, E, L, M, m0, BM, BN);
+    const int32_t pad = ui.pad;
+    const TileKeys tk = tile_keys(p, E, L, M, m0, BM, BN, pad);
     const int32_t key_lo = tk.key_lo, key_hi = tk.key_hi, c_base = tk.c_base, nchunk = tk.nchunk;
-    auto lo_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t { return row_lo(p, E, L, i); };
-    auto hi_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t { return row_hi(p, E, L, i); };
+    auto lo_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t { return row_lo(p, E, L, i, pad); };
+    auto hi_of = [&](int32_t i) __attribute__((always_inline)) -> int32_t { return row_hi(p, E, L, i, pad); };
     const int32_t cps = (nchunk + S - 1) / S;
     const int32_t c_first = split * cps;
     const int32_t c_end = min(nchunk, c_first + cps);

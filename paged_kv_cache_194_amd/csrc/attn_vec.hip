@@ -83,7 +83,7 @@ __device__ __forceinline__ int32_t vec_unit_blocks(const AttnParams& p, int32_t 
     const UnitInfo ui = load_unit(p, u);
     if (ui.q_len != 1 || ui.q_start < 0 || ui.q_start >= p.total_q) return -1;
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
-    const int32_t lo = (p.window > 0 && E - p.window > 0) ? E - p.window : 0;
+    const int32_t lo = single_row_lo(p, E, ui.pad);
     const int32_t b_end = (E + 15) >> 4, b_first = lo >> 4;
     return b_end > b_first ? b_end - b_first : 0;
 }
@@ -244,8 +244,9 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     const int32_t G = p.group;
     const int32_t Hkv = p.kv_heads;
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
-    // One query at position E-1: keys [lo, E) with the window's lower bound.
-    const int32_t lo = (p.window > 0 && E - p.window > 0) ? E - p.window : 0;
+    // One query at position E-1: keys [lo, E) with the window's and the
+    // left-padding lower bounds.
+    const int32_t lo = single_row_lo(p, E, ui.pad);
     const int32_t hi = E;
     const int32_t b_end = (hi + 15) >> 4;
     const int32_t b_first = lo >> 4;

@@ -25,6 +25,7 @@ struct AttnParams {
     const int32_t* seqused_k;
     const int32_t* block_table;
     const int32_t* seq_info;
+    const int32_t* kv_start;   // left-padding bound per unit, or null (none)
     const void* k_new;     // fused append (paged decode): [units, Hkv, D] or null
     const void* v_new;
     float* ws_o;           // split-K partial outputs [vec_wgs][Hkv][GT][D]
@@ -60,6 +61,7 @@ struct UnitInfo {
     int32_t q_len;
     int32_t kv_end;        // E after clamping
     int32_t col;           // column mode only
+    int32_t pad;           // left-padding bound (kv_start); <= 0: none
     bool keys_ok;          // column inside the store (column mode); true otherwise
 };
 
@@ -67,6 +69,7 @@ __device__ __forceinline__ UnitInfo load_unit(const AttnParams& p, int32_t u) {
     UnitInfo ui;
     ui.col = 0;
     ui.keys_ok = true;
+    ui.pad = p.kv_start ? p.kv_start[u] : 0;
     if (p.mode == kColumn) {
         const int32_t* s = p.seq_info + 4 * (int64_t)u;
         ui.q_start = s[0];
@@ -86,6 +89,16 @@ __device__ __forceinline__ UnitInfo load_unit(const AttnParams& p, int32_t u) {
         ui.kv_end = e < 0 ? 0 : (e > p.kv_cap ? p.kv_cap : e);
     }
     return ui;
+}
+
+// First key of a unit's single query row (position E - 1): the window's bound
+// and the left-padding bound; a row before the padding bound (a pad query)
+// keeps only its own key (tiny-llm kv_cache.py, padded_causal_mask).
+__device__ __forceinline__ int32_t single_row_lo(const AttnParams& p, int32_t E, int32_t pad) {
+    const int32_t lo = (p.window > 0 && E - p.window > 0) ? E - p.window : 0;
+    if (pad <= 0) return lo;
+    if (E - 1 < pad) return E > 1 ? E - 1 : 0;
+    return lo > pad ? lo : pad;
 }
 
 // ---- launchers (each returns hipGetLastError() of its launch) ----

@@ -55,14 +55,14 @@ def test_status_strings():
 def _decode(**over):
     args = dict(out=None, q=None, k=None, v=None, nb=4, bs=16, bt=None, mb=4, used=None, B=1,
                 msk=64, kn=None, vn=None, hq=8, hkv=2, d=128, scale=0.1, causal=0, window=0,
-                splits=0, ws=None, wsb=0, dtype=BF16)
+                pad=None, splits=0, ws=None, wsb=0, dtype=BF16)
     args.update(over)
     a = args
     return pkv.lib().pkv_paged_decode_attn(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"],
                                            a["bt"], a["mb"], a["used"], a["B"], a["msk"], a["kn"],
                                            a["vn"], a["hq"], a["hkv"], a["d"], a["scale"],
-                                           a["causal"], a["window"], a["splits"], a["ws"],
-                                           a["wsb"], a["dtype"], None)
+                                           a["causal"], a["window"], a["pad"], a["splits"],
+                                           a["ws"], a["wsb"], a["dtype"], None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -108,13 +108,13 @@ def test_workspace_too_small_is_rejected_before_launch():
 def _varlen(**over):
     a = dict(out=None, q=None, tq=4, k=None, v=None, cu=None, used=None, ns=1, bt=None, mb=4,
              nb=4, bs=16, si=None, nseg=0, rows=0, cols=0, mq=1, mk=64, hq=8, hkv=2, d=128,
-             scale=0.1, causal=0, window=0, splits=0, ws=None, wsb=0, dtype=BF16)
+             scale=0.1, causal=0, window=0, pad=None, splits=0, ws=None, wsb=0, dtype=BF16)
     a.update(over)
     return pkv.lib().pkv_varlen_attn(a["out"], a["q"], a["tq"], a["k"], a["v"], a["cu"], a["used"],
                                      a["ns"], a["bt"], a["mb"], a["nb"], a["bs"], a["si"], a["nseg"],
                                      a["rows"], a["cols"], a["mq"], a["mk"], a["hq"], a["hkv"],
-                                     a["d"], a["scale"], a["causal"], a["window"], a["splits"],
-                                     a["ws"], a["wsb"], a["dtype"], None)
+                                     a["d"], a["scale"], a["causal"], a["window"], a["pad"],
+                                     a["splits"], a["ws"], a["wsb"], a["dtype"], None)
 
 
 def test_varlen_host_errors():
