@@ -28,6 +28,18 @@ from . import BLOCK_SIZE, attn_workspace_bytes, paged_decode_attn, prefix_export
 BUCKETS = (512, 1024, 2048, 4096, 8192)
 TAIL_STEP = 2048
 
+_GRAPH_POOL = None
+
+
+def shared_graph_pool():
+    """One memory pool for every capture.  A private pool per capture table is
+    never handed back, and tables are rebuilt whenever the cache reallocates
+    (the pages measured about 40 MiB of growth per request that way)."""
+    global _GRAPH_POOL
+    if _GRAPH_POOL is None:
+        _GRAPH_POOL = torch.cuda.graph_pool_handle()
+    return _GRAPH_POOL
+
 
 def bucket_for(length: int) -> int:
     """Smallest bucket that holds ``length`` tokens; past the list, whole
@@ -188,7 +200,7 @@ class DecodeStepGraph:
                 self.forward()
         torch.cuda.current_stream(self.cache.device).wait_stream(side)
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        with torch.cuda.graph(graph, pool=shared_graph_pool()):
             self.forward()
         self.captures += 1
         self._graphs = {k: g for k, g in self._graphs.items() if k[1] == self.cache.generation}
@@ -200,3 +212,81 @@ class DecodeStepGraph:
         graph = self._graphs.get(key) or self._capture(key)
         graph.replay()
         return self.out
+
+
+class DecodeSession:
+    """Decode requests served one after another over one reusable paged cache.
+
+    vLLM-Omni paged_decode: one set of buffers behind an identity block table,
+    reused by whichever request fits them (``reusable_for``), so the captures
+    bound to those buffers survive from request to request.  Per request:
+    ``begin`` brings the prefill cache in -- ``load_prefix`` into the current
+    cache when it fits, else a new cache (``from_dynamic_cache``) with a new
+    capture table; each ``step`` advances the length by one token (growing at
+    a bucket edge, which bumps the generation and so the capture key), stages
+    the token's per-layer q / k_new / v_new and replays; ``end`` hands the K/V
+    back (``to_dynamic_cache``).  ``release`` drops buffers and captures.
+    """
+
+    def __init__(self, num_layers: int, q_heads: int, kv_heads: int, head_dim: int, device,
+                 dtype, num_splits: int = 0):
+        self.num_layers = num_layers
+        self.q_heads = q_heads
+        self.kv_heads = kv_heads
+        self.head_dim = head_dim
+        self.device = torch.device(device)
+        self.dtype = dtype
+        self.num_splits = num_splits
+        self.inputs = torch.zeros((num_layers, q_heads + 2 * kv_heads, head_dim), device=self.device,
+                                  dtype=dtype)
+        self.out = torch.zeros((num_layers, q_heads, head_dim), device=self.device, dtype=dtype)
+        self.cache: Optional[PagedDecodeCache] = None
+        self.runner: Optional[DecodeStepGraph] = None
+        self.requests = 0
+        self.reused = 0
+
+    def begin(self, keys: Sequence[Optional[torch.Tensor]],
+              values: Sequence[Optional[torch.Tensor]]) -> PagedDecodeCache:
+        """Start a request from its prefill cache (per layer ``[1, Hkv, S, D]``;
+        an empty one starts from length 0)."""
+        prefix = keys[0].shape[2] if keys and keys[0] is not None else 0
+        c = self.cache
+        if c is not None and c.reusable_for(self.num_layers, self.kv_heads, self.head_dim, self.dtype,
+                                            prefix + 1):
+            if not c.load_prefix(keys, values):
+                c.set_length(0)
+            self.reused += 1
+        else:
+            self.release()
+            c = PagedDecodeCache.from_dynamic_cache(keys, values, self.q_heads, self.device, self.dtype,
+                                                    num_splits=self.num_splits)
+            if c is None:
+                c = PagedDecodeCache(self.num_layers, self.q_heads, self.kv_heads, self.head_dim, 1,
+                                     self.device, self.dtype, num_splits=self.num_splits)
+            self.cache = c
+            self.runner = DecodeStepGraph(c, self.inputs, self.out)
+        self.requests += 1
+        return c
+
+    def step(self, token_inputs: torch.Tensor) -> torch.Tensor:
+        """One token: ``token_inputs`` ``[layers, Hq + 2 Hkv, D]`` (q, k_new,
+        v_new of every layer).  Returns the static ``[layers, Hq, D]`` output."""
+        c = self.cache
+        if c is None or self.runner is None:
+            raise RuntimeError("begin a request first")
+        n = c.length + 1
+        if n > c.bucket:
+            c.grow(n)
+        c.set_length(n)
+        self.inputs.copy_(token_inputs)
+        return self.runner.step()
+
+    def end(self) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+        if self.cache is None:
+            raise RuntimeError("no request in progress")
+        return self.cache.to_dynamic_cache()
+
+    def release(self) -> None:
+        """Drop the buffers and every capture bound to them."""
+        self.runner = None
+        self.cache = None

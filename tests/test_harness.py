@@ -1,5 +1,5 @@
-"""Host logic of the bucketed decode harness (no GPU): bucket schedule and the
-failure-atomic grow."""
+"""Host logic of the bucketed decode harness (no GPU): bucket schedule, the
+failure-atomic grow, and which request reuses the cache."""
 from __future__ import annotations
 
 import json
@@ -71,3 +71,33 @@ def test_set_length_rejects_lengths_past_the_bucket(monkeypatch):
     c = _cpu_cache()
     with pytest.raises(ValueError):
         c.set_length(513)
+
+
+def test_session_reuses_the_cache_while_requests_fit(monkeypatch):
+    """DecodeSession.begin: load into the current buffers when reusable_for
+    says the request fits, else new buffers and a new capture table.  The
+    library copies are replaced by recorders (no kernel runs on the CPU)."""
+    monkeypatch.setattr(harness, "attn_workspace_bytes", lambda *a, **k: 64)
+    copied = []
+    monkeypatch.setattr(harness, "prefix_import", lambda *a, **k: copied.append(a[5]))
+
+    class Runner:
+        def __init__(self, cache, inputs, out):
+            self.cache = cache
+
+    monkeypatch.setattr(harness, "DecodeStepGraph", Runner)
+    s = harness.DecodeSession(3, 8, 2, 64, "cpu", torch.bfloat16)
+
+    def prefill(n):
+        return [torch.zeros(1, 2, n, 64, dtype=torch.bfloat16)] * 3
+
+    c0 = s.begin(prefill(300), prefill(300))
+    r0 = s.runner
+    assert c0.bucket == 512 and c0.length == 300 and s.reused == 0
+    assert s.begin(prefill(100), prefill(100)) is c0 and s.runner is r0 and c0.length == 100
+    assert s.begin(prefill(511), prefill(511)) is c0                   # 512 keys still fit
+    c1 = s.begin(prefill(512), prefill(512))                           # the next token would not
+    assert c1 is not c0 and c1.bucket == 1024 and s.runner is not r0
+    assert s.begin([None], [None]) is c1 and c1.length == 0            # empty prefill: length 0
+    assert s.requests == 5 and s.reused == 3
+    assert copied == [300] * 3 + [100] * 3 + [511] * 3 + [512] * 3
