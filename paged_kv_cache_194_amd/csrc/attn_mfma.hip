@@ -217,9 +217,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             const int32_t per = (NI + 63) / 64;
             const int32_t ib = lane * per, ie = min(NI, ib + per);
             auto item_n = [&](int32_t it) { return mfma_item_chunks(p, it / T, it - (it / T) * T, BM, BN); };
-            const int32_t c = deal_size(item_n, ib, ie, (int64_t)p.mfma_splits * NI);
+            const DealItems items = deal_items(item_n, ib, ie);
+            const int32_t c = deal_size(items, item_n, (int64_t)p.mfma_splits * NI);
             int32_t cnt = 0;
-            for (int32_t it = ib; it < ie; ++it) cnt += deal_slots_of(item_n(it), c);
+            deal_for_each(items, item_n, [&](int32_t, int32_t n) { cnt += deal_slots_of(n, c); });
             int32_t incl = cnt;
 #pragma unroll
             for (int st = 1; st < 64; st *= 2) {
@@ -229,13 +230,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             if (lane == 0) sWork[0] = -1;
             int32_t acc = incl - cnt;
             const int32_t w = blockIdx.y;
-            for (int32_t it = ib; it < ie; ++it) {
-                const int32_t k = deal_slots_of(item_n(it), c);
+            deal_for_each(items, item_n, [&](int32_t it, int32_t n) {
+                const int32_t k = deal_slots_of(n, c);
                 if (w >= acc && w < acc + k) {
                     sWork[0] = it / T; sWork[1] = it - (it / T) * T; sWork[2] = w - acc; sWork[3] = k; sWork[4] = acc;
                 }
                 acc += k;
-            }
+            });
         }
         __syncthreads();
         u = sWork[0]; tile = sWork[1]; split = sWork[2]; S = sWork[3]; slot0 = sWork[4];

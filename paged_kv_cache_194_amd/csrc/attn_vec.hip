@@ -211,9 +211,10 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             const int32_t per = (U + 63) / 64;
             const int32_t ub = lane * per, ue = min(U, ub + per);
             auto unit_n = [&](int32_t uu) { return vec_unit_blocks(p, uu); };
-            const int32_t c = deal_size(unit_n, ub, ue, W);
+            const DealItems items = deal_items(unit_n, ub, ue);
+            const int32_t c = deal_size(items, unit_n, W);
             int32_t cnt = 0;
-            for (int32_t uu = ub; uu < ue; ++uu) cnt += deal_slots_of(vec_unit_blocks(p, uu), c);
+            deal_for_each(items, unit_n, [&](int32_t, int32_t n) { cnt += deal_slots_of(n, c); });
             int32_t incl = cnt;
 #pragma unroll
             for (int st = 1; st < 64; st *= 2) {
@@ -223,13 +224,13 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             if (lane == 0) sWork[0] = -1;
             int32_t acc = incl - cnt;
             const int32_t w = slot;
-            for (int32_t uu = ub; uu < ue; ++uu) {
-                const int32_t n = deal_slots_of(vec_unit_blocks(p, uu), c);
+            deal_for_each(items, unit_n, [&](int32_t uu, int32_t nb) {
+                const int32_t n = deal_slots_of(nb, c);
                 if (w >= acc && w < acc + n) {
                     sWork[0] = uu; sWork[1] = w - acc; sWork[2] = n; sWork[3] = acc;
                 }
                 acc += n;
-            }
+            });
         }
         __syncthreads();
         u = sWork[0]; split = sWork[1]; S = sWork[2]; slot0 = sWork[3];

@@ -166,17 +166,43 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 __device__ __forceinline__ int32_t deal_slots_of(int32_t n, int32_t c) {
     return n < 0 ? 0 : (n <= c ? 1 : (n + c - 1) / c);
 }
+
+// The dealing wave's lane owns items [ib, ie).  Their counts are read once
+// (each read is a chain of global loads) and kept in registers for the first
+// kDealRegs items; any further items of a lane are read again per pass.
+constexpr int kDealRegs = 8;
+struct DealItems {
+    int32_t ib, ie;
+    int32_t n[kDealRegs];
+};
 template <typename F>
-__device__ int32_t deal_size(const F& item_n, int32_t ib, int32_t ie, int64_t slots) {
+__device__ __forceinline__ DealItems deal_items(const F& item_n, int32_t ib, int32_t ie) {
+    DealItems d;
+    d.ib = ib;
+    d.ie = ie;
+#pragma unroll
+    for (int k = 0; k < kDealRegs; ++k) d.n[k] = (ib + k < ie) ? item_n(ib + k) : 0;
+    return d;
+}
+// body(item, count) for each of the lane's items, in order.
+template <typename F, typename B>
+__device__ __forceinline__ void deal_for_each(const DealItems& d, const F& item_n, const B& body) {
+#pragma unroll
+    for (int k = 0; k < kDealRegs; ++k)
+        if (d.ib + k < d.ie) body(d.ib + k, d.n[k]);
+    for (int32_t i = d.ib + kDealRegs; i < d.ie; ++i) body(i, item_n(i));
+}
+template <typename F>
+__device__ int32_t deal_size(const DealItems& d, const F& item_n, int64_t slots) {
     int32_t nmax = 0;
-    for (int32_t i = ib; i < ie; ++i) nmax = max(nmax, item_n(i));
+    deal_for_each(d, item_n, [&](int32_t, int32_t n) { nmax = max(nmax, n); });
 #pragma unroll
     for (int st = 1; st < 64; st *= 2) nmax = max(nmax, __shfl_xor(nmax, st, 64));
     int32_t lo = 1, hi = nmax > 1 ? nmax : 1;      // c = nmax gives one slot per item
     while (lo < hi) {                              // wave-uniform loop
         const int32_t c = lo + (hi - lo) / 2;
         int64_t k = 0;
-        for (int32_t i = ib; i < ie; ++i) k += deal_slots_of(item_n(i), c);
+        deal_for_each(d, item_n, [&](int32_t, int32_t n) { k += deal_slots_of(n, c); });
 #pragma unroll
         for (int st = 1; st < 64; st *= 2) k += __shfl_xor(k, st, 64);
         if (k <= slots) hi = c; else lo = c + 1;
