@@ -170,8 +170,17 @@ __device__ __forceinline__ void merge_splits(const AttnParams& p, int32_t g, int
     }
 }
 
+// Waves per SIMD the register budget is held to: two (at most 256 VGPRs) for
+// the shapes that fit -- the pipelined block loop otherwise grows past that
+// and halves occupancy -- one for the large ones (head_dim 256, a group of 8,
+// fp32 above head_dim 64), which spill when held to 256.
+template <typename T, int D, int GT>
+constexpr int vec_waves_per_simd() {
+    return (sizeof(T) == 2 ? (D <= 128 && GT <= 4) : (D <= 64 && GT <= 4)) ? 2 : 1;
+}
+
 template <typename T, int D, int GT, bool PAGED>
-__global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void attn_vec_kernel(AttnParams p) {
     using C = VecCfg<T, D, GT>;
     constexpr int EB = C::EB, VEC = C::VEC, KLPT = C::KLPT, KCH = C::KCH, KTPW = C::KTPW,
                   KNI = C::KNI, VLPT = C::VLPT, VTPW = C::VTPW, VNI = C::VNI;
@@ -312,51 +321,40 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
             return (int64_t)r * col_stride + (int64_t)ui.col * tok_stride + head_off;
         }
     };
-    auto block_id = [&](int i) -> int32_t {
-        if constexpr (!PAGED) return 0;
-        if ((i & 63) == 0 && i > 0) {           // gather the next 64 ids
-            const int32_t blk = first + kWaves * (i + lane);
-            ids = blk < se ? p.block_table[(int64_t)u * p.max_blocks + blk] : -1;
-        }
-        return __builtin_amdgcn_readlane(ids, i & 63);
-    };
     auto id_ok = [&](int32_t id) { return !PAGED || (id >= 0 && id < p.num_blocks); };
 
+    // Every load of the block loop is issued unconditionally -- a block with
+    // no storage loads pool block 0 and is skipped when processed -- so the
+    // compiler's wait counts see the same loads on every path and wait only
+    // for the block being processed, never for the one in flight behind it.
     auto load = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
         const int32_t blk = first + kWaves * i;
-        if (!id_ok(id)) return;
+        const int32_t idc = id_ok(id) ? id : 0;
 #pragma unroll
         for (int j = 0; j < KNI; ++j) {
             const int tt = j * KTPW + ktok;
-            const int64_t a = tok_addr(blk, id, tt);
+            const int64_t a = tok_addr(blk, idc, tt);
 #pragma unroll
             for (int c = 0; c < KCH; ++c) kr[j][c] = ld16_stream(Kb + a + (kpart + KLPT * c) * 16);
         }
 #pragma unroll
-        for (int j = 0; j < VNI; ++j) vr[j] = ld16_stream(Vb + tok_addr(blk, id, j * VTPW + vtok) + vpart * 16);
-        if (fuse && blk == (pn >> 4)) {         // this step's token: from k_new, and stored
-            uint8_t* Kw = (uint8_t*)p.k;
-            uint8_t* Vw = (uint8_t*)p.v;
-#pragma unroll
-            for (int j = 0; j < KNI; ++j) {
-                if (j * KTPW + ktok == (pn & 15)) {
-                    const int64_t a = tok_addr(blk, id, pn & 15);
-#pragma unroll
-                    for (int c = 0; c < KCH; ++c) {
-                        kr[j][c] = ld16(kn + (kpart + KLPT * c) * 16);
-                        st16(Kw + a + (kpart + KLPT * c) * 16, kr[j][c]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < VNI; ++j) {
-                if (j * VTPW + vtok == (pn & 15)) {
-                    vr[j] = ld16(vn + vpart * 16);
-                    st16(Vw + tok_addr(blk, id, pn & 15) + vpart * 16, vr[j]);
-                }
-            }
-        }
+        for (int j = 0; j < VNI; ++j) vr[j] = ld16_stream(Vb + tok_addr(blk, idc, j * VTPW + vtok) + vpart * 16);
     };
+
+    // Fused append.  Position E-1 sits in the last live block, which is the
+    // last block of the one wave that owns it.  That wave writes this step's
+    // row to its slot before the loop, leaves the block out of the loop, and
+    // processes it after the loop with the row taken from k_new / v_new in
+    // registers (whatever the cache load returned for it).
+    const int32_t pblk = pn >> 4, ptt = pn & 15;
+    const bool own_new = fuse && pblk >= sb && pblk < se && (pblk - sb) % kWaves == wave;
+    const int32_t pid = (own_new && PAGED) ? p.block_table[(int64_t)u * p.max_blocks + pblk] : 0;
+    if (own_new && id_ok(pid) && lane < D * EB / 16) {
+        const int64_t a = tok_addr(pblk, pid, ptt);
+        st16((uint8_t*)p.k + a + lane * 16, ld16(kn + lane * 16));
+        st16((uint8_t*)p.v + a + lane * 16, ld16(vn + lane * 16));
+    }
+    const int nb_loop = own_new ? nb - 1 : nb;
 
     float* P = sP[wave];
     auto process = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
@@ -479,25 +477,52 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     };
 
     // ---- block loop, next block's loads in flight during the current compute ----
+    // Groups of up to 64 blocks per wave: lane l holds the pool id of the
+    // group's l-th block (the first group's ids were read above).
     {
         u32x4 ka[KNI][KCH], kb[KNI][KCH], va[VNI], vb[VNI];
-        int32_t ida = 0, idb = 0;
-        if (nb > 0) {
-            ida = block_id(0);
-            load(0, ida, ka, va);
+        for (int g0 = 0; g0 < nb_loop; g0 += 64) {
+            const int gn = min(64, nb_loop - g0);
+            if constexpr (PAGED) {
+                if (g0 > 0) {
+                    const int32_t blk = first + kWaves * (g0 + lane);
+                    ids = lane < gn ? p.block_table[(int64_t)u * p.max_blocks + blk] : -1;
+                }
+            }
+            auto id_of = [&](int k) -> int32_t { return PAGED ? __builtin_amdgcn_readlane(ids, k) : 0; };
+            int32_t ida = id_of(0), idb = 0;
+            load(g0, ida, ka, va);
+            int k = 0;
+            for (; k + 2 < gn; k += 2) {
+                idb = id_of(k + 1);
+                load(g0 + k + 1, idb, kb, vb);
+                process(g0 + k, ida, ka, va);
+                ida = id_of(k + 2);
+                load(g0 + k + 2, ida, ka, va);
+                process(g0 + k + 1, idb, kb, vb);
+            }
+            if (k + 1 < gn) {
+                idb = id_of(k + 1);
+                load(g0 + k + 1, idb, kb, vb);
+                process(g0 + k, ida, ka, va);
+                process(g0 + k + 1, idb, kb, vb);
+            } else {
+                process(g0 + k, ida, ka, va);
+            }
         }
-        for (int i = 0; i < nb; i += 2) {
-            if (i + 1 < nb) {
-                idb = block_id(i + 1);
-                load(i + 1, idb, kb, vb);
-            }
-            process(i, ida, ka, va);
-            if (i + 1 >= nb) break;
-            if (i + 2 < nb) {
-                ida = block_id(i + 2);
-                load(i + 2, ida, ka, va);
-            }
-            process(i + 1, idb, kb, vb);
+        if (own_new) {
+            const int i = nb - 1;
+            load(i, pid, ka, va);
+#pragma unroll
+            for (int j = 0; j < KNI; ++j)
+                if (j * KTPW + ktok == ptt) {
+#pragma unroll
+                    for (int c = 0; c < KCH; ++c) ka[j][c] = ld16(kn + (kpart + KLPT * c) * 16);
+                }
+#pragma unroll
+            for (int j = 0; j < VNI; ++j)
+                if (j * VTPW + vtok == ptt) va[j] = ld16(vn + vpart * 16);
+            process(i, pid, ka, va);
         }
     }
 
