@@ -130,7 +130,8 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  *                takes more of them.  Results of different split counts agree to
  *                rounding; the same inputs and split count give the same bits.
  *                The library's own choice depends on the current device's
- *                compute-unit count for multi-row units.
+ *                compute-unit count for a single sequence and for multi-row
+ *                units.
  * workspace    : device scratch of at least pkv_attn_workspace_bytes(num_seqs, 1,
  *                max_seqlen_k, q_heads, kv_heads, head_dim, num_splits) bytes
  *                (may be NULL when that is 0).  Zero-fill it once before its
