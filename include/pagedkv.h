@@ -242,6 +242,77 @@ pkv_status pkv_prefix_export(void* k_dst, void* v_dst, const void* k_cache, cons
                              int32_t kv_heads, int32_t head_dim, pkv_dtype dtype, void* stream);
 
 /*
+ * Batched-sequence column store: host bookkeeping (BatchControl).
+ * (ExecuTorch PR #24073, the batched-sequence cache: one column per admitted
+ * sequence of a [rows, max_seqs + 1, H, D] store, the last column scratch for
+ * padded static-width writes; ring layers of min(capacity, window +
+ * max_write - 1) rows; declare_step / prepare_step / commit_step, seq_clone,
+ * seq_rm, rewind bounded by the ring floor, pos, max_seqs; one contiguous run
+ * of tokens per owner in a step.  PR #24076: a ring grows like a flat store
+ * until it first wraps, capped at its own rows.)
+ *
+ * The object lives on the host and touches no device memory: prepare_step
+ * fills caller-owned host buffers that the caller uploads, and the device part
+ * of a clone is pkv_column_copy.  A sequence id is its column.  Not thread-safe.
+ *
+ * pkv_batch_create : a ring store when window > 0 and window + max_write - 1 <=
+ *                    capacity (rows = that sum, positions unbounded, slot of
+ *                    position p in column c = (p % rows) * cols + c); otherwise
+ *                    a flat store of `capacity` rows (a column is full at
+ *                    capacity).  NULL on bad arguments (pkv_last_error says why).
+ * pkv_batch_rows_needed : store rows a step of `step_width` tokens needs now,
+ *                    rounded up to `row_step`, at most the store's rows (the
+ *                    growth schedule of a flat store, or of a ring not yet
+ *                    wrapped).
+ * pkv_batch_seq_new : the lowest free column; PKV_EINVAL when all are taken.
+ * pkv_batch_seq_clone : a new sequence at the source's position; *copy_rows
+ *                    store rows of the source column hold its live keys and
+ *                    must be copied (pkv_column_copy, every layer) before the
+ *                    clone is used.
+ * pkv_batch_rewind : move a sequence back to `pos`; PKV_EINVAL past its position
+ *                    or below pkv_batch_floor (a ring must still hold the keys
+ *                    a step starting at `pos` can see).
+ * pkv_batch_declare_step : this step's owners in row order, n_tokens[i] in
+ *                    1 .. max_write each, every owner at most once, their sum
+ *                    <= width (the static token width of the step).
+ * pkv_batch_prepare_step : seq_info [max_segments, 4] = (q_start, q_len, col,
+ *                    kv_end = pos + q_len) per owner, zero rows after them; slots
+ *                    int64 [width]: token t of an owner at position pos + t goes
+ *                    to its column's slot, padding tokens to the scratch column.
+ *                    Feed them to pkv_kv_append and pkv_varlen_attn (seq_info).
+ * pkv_batch_commit_step : advances every owner by its tokens.
+ * seq_new / seq_rm / seq_clone / rewind are refused between declare and commit.
+ */
+typedef struct pkv_batch pkv_batch;
+pkv_batch* pkv_batch_create(int32_t max_seqs, int32_t capacity, int32_t window, int32_t max_write);
+void pkv_batch_destroy(pkv_batch* b);
+int32_t pkv_batch_max_seqs(const pkv_batch* b);
+int32_t pkv_batch_cols(const pkv_batch* b);
+int32_t pkv_batch_rows(const pkv_batch* b);
+int32_t pkv_batch_rows_needed(const pkv_batch* b, int32_t step_width, int32_t row_step);
+pkv_status pkv_batch_seq_new(pkv_batch* b, int32_t* seq);
+pkv_status pkv_batch_seq_rm(pkv_batch* b, int32_t seq);
+pkv_status pkv_batch_seq_clone(pkv_batch* b, int32_t src, int32_t* dst, int32_t* copy_rows);
+pkv_status pkv_batch_rewind(pkv_batch* b, int32_t seq, int32_t pos);
+pkv_status pkv_batch_pos(const pkv_batch* b, int32_t seq, int32_t* pos);
+int32_t pkv_batch_floor(const pkv_batch* b, int32_t seq);
+pkv_status pkv_batch_declare_step(pkv_batch* b, const int32_t* seqs, const int32_t* n_tokens,
+                                  int32_t count, int32_t width);
+pkv_status pkv_batch_prepare_step(pkv_batch* b, int32_t* seq_info, int32_t max_segments,
+                                  int64_t* slots, int32_t* num_segments);
+pkv_status pkv_batch_commit_step(pkv_batch* b);
+
+/*
+ * pkv_column_copy -- copy store rows [0, n_rows) of column src_col to column
+ * dst_col in K and V (the device half of seq_clone).
+ * k, v : [rows, cols, kv_heads, head_dim], 16-byte aligned.  Raw words move.
+ * src_col == dst_col or n_rows == 0 enqueues nothing.
+ */
+pkv_status pkv_column_copy(void* k, void* v, int32_t rows, int32_t cols, int32_t kv_heads,
+                           int32_t head_dim, int32_t src_col, int32_t dst_col, int32_t n_rows,
+                           pkv_dtype dtype, void* stream);
+
+/*
  * pkv_attn_workspace_bytes -- device scratch an attention call with these host
  * arguments needs (split-K partials); 0 when it needs none.  `units` is num_seqs
  * (paged) or num_segments (column); num_splits as passed to the call.  With

@@ -16,8 +16,8 @@ import torch
 
 __all__ = [
     "PagedKVError", "BLOCK_SIZE", "lib", "library_path", "kv_append", "paged_decode_attn",
-    "varlen_attn", "prefix_import", "prefix_export", "attn_workspace_bytes", "attn_num_splits",
-    "status_string", "last_error", "EXPORTED_SYMBOLS",
+    "varlen_attn", "prefix_import", "prefix_export", "column_copy", "BatchControl",
+    "attn_workspace_bytes", "attn_num_splits", "status_string", "last_error", "EXPORTED_SYMBOLS",
 ]
 
 BLOCK_SIZE = 16
@@ -30,7 +30,10 @@ _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED_SYMBOLS = (
     "pkv_kv_append", "pkv_paged_decode_attn", "pkv_varlen_attn", "pkv_prefix_import",
     "pkv_prefix_export", "pkv_attn_workspace_bytes", "pkv_attn_num_splits", "pkv_status_string",
-    "pkv_last_error",
+    "pkv_last_error", "pkv_batch_create", "pkv_batch_destroy", "pkv_batch_max_seqs", "pkv_batch_cols",
+    "pkv_batch_rows", "pkv_batch_rows_needed", "pkv_batch_seq_new", "pkv_batch_seq_rm",
+    "pkv_batch_seq_clone", "pkv_batch_rewind", "pkv_batch_pos", "pkv_batch_floor",
+    "pkv_batch_declare_step", "pkv_batch_prepare_step", "pkv_batch_commit_step", "pkv_column_copy",
 )
 
 
@@ -62,6 +65,22 @@ _SIGS = {
                                  _i32, _i32, _i32, _vp]),
     "pkv_prefix_export": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32,
                                  _i32, _vp]),
+    "pkv_batch_create": (_vp, [_i32, _i32, _i32, _i32]),
+    "pkv_batch_destroy": (None, [_vp]),
+    "pkv_batch_max_seqs": (_i32, [_vp]),
+    "pkv_batch_cols": (_i32, [_vp]),
+    "pkv_batch_rows": (_i32, [_vp]),
+    "pkv_batch_rows_needed": (_i32, [_vp, _i32, _i32]),
+    "pkv_batch_seq_new": (_i32, [_vp, _vp]),
+    "pkv_batch_seq_rm": (_i32, [_vp, _i32]),
+    "pkv_batch_seq_clone": (_i32, [_vp, _i32, _vp, _vp]),
+    "pkv_batch_rewind": (_i32, [_vp, _i32, _i32]),
+    "pkv_batch_pos": (_i32, [_vp, _i32, _vp]),
+    "pkv_batch_floor": (_i32, [_vp, _i32]),
+    "pkv_batch_declare_step": (_i32, [_vp, _vp, _vp, _i32, _i32]),
+    "pkv_batch_prepare_step": (_i32, [_vp, _vp, _i32, _vp, _vp]),
+    "pkv_batch_commit_step": (_i32, [_vp]),
+    "pkv_column_copy": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_attn_num_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -185,6 +204,96 @@ def prefix_export(k_dst: torch.Tensor, v_dst: torch.Tensor, k_cache: torch.Tenso
     _check(lib().pkv_prefix_export(_ptr(k_dst), _ptr(v_dst), _ptr(k_cache), _ptr(v_cache), nb,
                                    BLOCK_SIZE, B, n, _ptr(block_table), block_table.shape[1], H, D,
                                    _dtype(k_cache), _stream(k_cache)))
+
+
+def column_copy(k_store: torch.Tensor, v_store: torch.Tensor, src_col: int, dst_col: int,
+                n_rows: int) -> None:
+    """Copy store rows ``[:n_rows]`` of column ``src_col`` to ``dst_col`` in
+    ``[rows, cols, Hkv, D]`` K and V stores."""
+    _dev(k_store, v_store)
+    _need(k_store.dim() == 4 and k_store.shape == v_store.shape and k_store.dtype == v_store.dtype,
+          "stores must be equal [rows, cols, Hkv, D]")
+    rows, cols, H, D = k_store.shape
+    _check(lib().pkv_column_copy(_ptr(k_store), _ptr(v_store), rows, cols, H, D, int(src_col),
+                                 int(dst_col), int(n_rows), _dtype(k_store), _stream(k_store)))
+
+
+class BatchControl:
+    """Host bookkeeping of a batched-sequence column store (one column per
+    sequence, the last one scratch); see ``pkv_batch_*`` in the C header.
+
+    ``prepare_step`` returns ``(seq_info, slots, num_segments)`` as host
+    tensors (int32 ``[2 * max_seqs, 4]``, int64 ``[width]``) ready to be moved
+    to the device for ``kv_append`` and ``varlen_attn``."""
+
+    def __init__(self, max_seqs: int, capacity: int, window: int = 0, max_write: int = 1):
+        h = lib().pkv_batch_create(max_seqs, capacity, window, max_write)
+        if not h:
+            raise PagedKVError(PKV_EINVAL, last_error())
+        self._h = ctypes.c_void_p(h)
+        self.max_seqs = int(lib().pkv_batch_max_seqs(self._h))
+        self.cols = int(lib().pkv_batch_cols(self._h))
+        self.rows = int(lib().pkv_batch_rows(self._h))
+        self.max_segments = 2 * self.max_seqs
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _LIB is not None:
+            _LIB.pkv_batch_destroy(h)
+            self._h = None
+
+    def _out(self, fn, *args) -> int:
+        v = ctypes.c_int32(0)
+        _check(fn(self._h, *args, ctypes.byref(v)))
+        return int(v.value)
+
+    def seq_new(self) -> int:
+        return self._out(lib().pkv_batch_seq_new)
+
+    def seq_rm(self, seq: int) -> None:
+        _check(lib().pkv_batch_seq_rm(self._h, int(seq)))
+
+    def seq_clone(self, src: int, stores=()) -> int:
+        """A new sequence at ``src``'s position; ``stores`` lists the
+        ``(k_store, v_store)`` of every layer whose column is copied."""
+        dst, rows = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pkv_batch_seq_clone(self._h, int(src), ctypes.byref(dst), ctypes.byref(rows)))
+        for k, v in stores:
+            column_copy(k, v, src, dst.value, rows.value)
+        return int(dst.value)
+
+    def rewind(self, seq: int, pos: int) -> None:
+        _check(lib().pkv_batch_rewind(self._h, int(seq), int(pos)))
+
+    def pos(self, seq: int) -> int:
+        return self._out(lib().pkv_batch_pos, int(seq))
+
+    def floor(self, seq: int) -> int:
+        return int(lib().pkv_batch_floor(self._h, int(seq)))
+
+    def rows_needed(self, step_width: int, row_step: int = 256) -> int:
+        return int(lib().pkv_batch_rows_needed(self._h, int(step_width), int(row_step)))
+
+    def declare_step(self, seqs, n_tokens, width: Optional[int] = None) -> None:
+        seqs = [int(x) for x in seqs]
+        n_tokens = [int(x) for x in n_tokens]
+        _need(len(seqs) == len(n_tokens), "one token count per sequence")
+        width = sum(n_tokens) if width is None else int(width)
+        a = (ctypes.c_int32 * max(1, len(seqs)))(*seqs)
+        b = (ctypes.c_int32 * max(1, len(n_tokens)))(*n_tokens)
+        _check(lib().pkv_batch_declare_step(self._h, a, b, len(seqs), width))
+        self._width = width
+
+    def prepare_step(self):
+        info = torch.zeros((self.max_segments, 4), dtype=torch.int32)
+        slots = torch.zeros((max(1, self._width),), dtype=torch.int64)[:self._width]
+        n = ctypes.c_int32(0)
+        _check(lib().pkv_batch_prepare_step(self._h, ctypes.c_void_p(info.data_ptr()), self.max_segments,
+                                            ctypes.c_void_p(slots.data_ptr()), ctypes.byref(n)))
+        return info, slots, int(n.value)
+
+    def commit_step(self) -> None:
+        _check(lib().pkv_batch_commit_step(self._h))
 
 
 def attn_workspace_bytes(units: int, max_seqlen_q: int, max_seqlen_k: int, q_heads: int,

@@ -7,8 +7,20 @@
 #include "internal.h"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
+
+namespace pkv {
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+}
+void clear_error() { g_last_error[0] = '\0'; }
+}  // namespace pkv
+
+namespace {
 
 pkv_status fail(pkv_status s, const char* fmt, ...) {
     va_list ap;
@@ -19,7 +31,7 @@ pkv_status fail(pkv_status s, const char* fmt, ...) {
 }
 
 pkv_status ok() {
-    g_last_error[0] = '\0';
+    pkv::clear_error();
     return PKV_OK;
 }
 

@@ -101,6 +101,10 @@ __device__ __forceinline__ int32_t single_row_lo(const AttnParams& p, int32_t E,
     return lo > pad ? lo : pad;
 }
 
+// Text for pkv_last_error() on the calling thread.
+void set_error(const char* fmt, ...);
+void clear_error();
+
 // ---- launchers (each returns hipGetLastError() of its launch) ----
 
 hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
