@@ -79,14 +79,15 @@ int32_t device_cus() {
 // Vector path, at least 8 blocks (two per wave) per split.  Several units:
 // about 2048 work groups (four dispatch rounds at two per CU; the balanced
 // deal keeps them even; the 64-sequence batch measured 207 us against 214 us
-// at 1024).  One unit: about 3/4 of the CUs -- one short round, where
-// every split's work group is on the critical path (the 4096-key, 8-head
-// decode step measured 446 us at 24 splits against 463 us at 32).
+// at 1024).  One unit: one work group per CU -- a single short round in which
+// every split's work group is on the critical path, each wave with the same
+// number of blocks where the length allows (the 4096-key, 8-head decode step
+// measured 434 us at 32 splits, 448 us at 24, 456 us at 28, 504 us at 36).
 int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_splits) {
     if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
     const int64_t base = (int64_t)(units > 0 ? units : 1) * kv_heads;
     const int64_t blocks = ((int64_t)(keys > 0 ? keys : 1) + 15) / 16;
-    const int64_t target = units <= 1 ? (int64_t)device_cus() * 3 / 4 : 2048;
+    const int64_t target = units <= 1 ? (int64_t)device_cus() : 2048;
     return clamp_splits((target + base - 1) / base, blocks / 8 > 0 ? blocks / 8 : 1);
 }
 

@@ -327,25 +327,11 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     // no storage loads pool block 0 and is skipped when processed -- so the
     // compiler's wait counts see the same loads on every path and wait only
     // for the block being processed, never for the one in flight behind it.
-    auto load = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
-        const int32_t blk = first + kWaves * i;
-        const int32_t idc = id_ok(id) ? id : 0;
-#pragma unroll
-        for (int j = 0; j < KNI; ++j) {
-            const int tt = j * KTPW + ktok;
-            const int64_t a = tok_addr(blk, idc, tt);
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) kr[j][c] = ld16_stream(Kb + a + (kpart + KLPT * c) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < VNI; ++j) vr[j] = ld16_stream(Vb + tok_addr(blk, idc, j * VTPW + vtok) + vpart * 16);
-    };
-
     // Fused append.  Position E-1 sits in the last live block, which is the
     // last block of the one wave that owns it.  That wave writes this step's
-    // row to its slot before the loop, leaves the block out of the loop, and
-    // processes it after the loop with the row taken from k_new / v_new in
-    // registers (whatever the cache load returned for it).
+    // row to its slot before the loop; inside the loop, the lanes that would
+    // read that row from the cache read it from k_new / v_new instead (an
+    // address choice, so the block stays in the load pipeline like any other).
     const int32_t pblk = pn >> 4, ptt = pn & 15;
     const bool own_new = fuse && pblk >= sb && pblk < se && (pblk - sb) % kWaves == wave;
     const int32_t pid = (own_new && PAGED) ? p.block_table[(int64_t)u * p.max_blocks + pblk] : 0;
@@ -354,7 +340,27 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
         st16((uint8_t*)p.k + a + lane * 16, ld16(kn + lane * 16));
         st16((uint8_t*)p.v + a + lane * 16, ld16(vn + lane * 16));
     }
-    const int nb_loop = own_new ? nb - 1 : nb;
+
+    auto load = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
+        const int32_t blk = first + kWaves * i;
+        const int32_t idc = id_ok(id) ? id : 0;
+        const bool own = own_new && blk == pblk;        // wave-uniform
+#pragma unroll
+        for (int j = 0; j < KNI; ++j) {
+            const int tt = j * KTPW + ktok;
+            const uint8_t* src = Kb + tok_addr(blk, idc, tt) + kpart * 16;
+            if (own && tt == ptt) src = kn + kpart * 16;
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) kr[j][c] = ld16_stream(src + KLPT * c * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < VNI; ++j) {
+            const int tt = j * VTPW + vtok;
+            const uint8_t* src = Vb + tok_addr(blk, idc, tt) + vpart * 16;
+            if (own && tt == ptt) src = vn + vpart * 16;
+            vr[j] = ld16_stream(src);
+        }
+    };
 
     float* P = sP[wave];
     auto process = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
@@ -481,8 +487,8 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     // group's l-th block (the first group's ids were read above).
     {
         u32x4 ka[KNI][KCH], kb[KNI][KCH], va[VNI], vb[VNI];
-        for (int g0 = 0; g0 < nb_loop; g0 += 64) {
-            const int gn = min(64, nb_loop - g0);
+        for (int g0 = 0; g0 < nb; g0 += 64) {
+            const int gn = min(64, nb - g0);
             if constexpr (PAGED) {
                 if (g0 > 0) {
                     const int32_t blk = first + kWaves * (g0 + lane);
@@ -509,20 +515,6 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
             } else {
                 process(g0 + k, ida, ka, va);
             }
-        }
-        if (own_new) {
-            const int i = nb - 1;
-            load(i, pid, ka, va);
-#pragma unroll
-            for (int j = 0; j < KNI; ++j)
-                if (j * KTPW + ktok == ptt) {
-#pragma unroll
-                    for (int c = 0; c < KCH; ++c) ka[j][c] = ld16(kn + (kpart + KLPT * c) * 16);
-                }
-#pragma unroll
-            for (int j = 0; j < VNI; ++j)
-                if (j * VTPW + vtok == ptt) va[j] = ld16(vn + vpart * 16);
-            process(i, pid, ka, va);
         }
     }
 
