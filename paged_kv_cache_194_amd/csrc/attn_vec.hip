@@ -49,9 +49,13 @@ struct VecCfg {
     static constexpr int VEC = 16 / EB;       // elements per 16-byte chunk
     static constexpr int RC = D / VEC;        // chunks per token row of one head
     static constexpr int qdw(int klpt) { return GT * (RC / klpt) * 4; }
-    // Lanes per token in the K layout: the fewest that keep q in <= 64 dwords.
-    static constexpr int KLPT = (RC >= 4 && qdw(4) <= 64) ? 4
-                              : (RC >= 8 && qdw(8) <= 64) ? 8
+    // Lanes per token in the K layout: the fewest that keep q in <= 64 dwords,
+    // but at least 8 where a row has 8 chunks, so that one load instruction
+    // covers whole 128-byte lines of its tokens (with 4 lanes per token each
+    // line was requested by two instructions, half a line each: the batched
+    // 64-sequence decode streamed about 10 % slower).
+    static constexpr int KLPT = (RC >= 8 && qdw(8) <= 64) ? 8
+                              : (RC >= 4 && RC < 8 && qdw(4) <= 64) ? 4
                               : (RC >= 16 && qdw(16) <= 64) ? 16
                               : (RC >= 32 && qdw(32) <= 64) ? 32 : RC;
     static constexpr int KCH = RC / KLPT;     // chunks per lane per token
@@ -328,18 +332,26 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     // compiler's wait counts see the same loads on every path and wait only
     // for the block being processed, never for the one in flight behind it.
     // Fused append.  Position E-1 sits in the last live block, which is the
-    // last block of the one wave that owns it.  That wave writes this step's
-    // row to its slot before the loop; inside the loop, the lanes that would
-    // read that row from the cache read it from k_new / v_new instead (an
-    // address choice, so the block stays in the load pipeline like any other).
+    // last block of the one wave that owns it.  Inside the loop, the lanes of
+    // that wave that would read the row from the cache read it from k_new /
+    // v_new instead (an address choice, so the block stays in the load
+    // pipeline like any other).  No other work group reads that row in this
+    // call, so the wave may write it to its slot at either end of the loop:
+    // after it where registers are to spare (the store's waits then never
+    // delay the first block's loads), before it for the shapes held to one
+    // wave per SIMD (whose loop would otherwise carry the store's operands).
     const int32_t pblk = pn >> 4, ptt = pn & 15;
     const bool own_new = fuse && pblk >= sb && pblk < se && (pblk - sb) % kWaves == wave;
     const int32_t pid = (own_new && PAGED) ? p.block_table[(int64_t)u * p.max_blocks + pblk] : 0;
-    if (own_new && id_ok(pid) && lane < D * EB / 16) {
-        const int64_t a = tok_addr(pblk, pid, ptt);
-        st16((uint8_t*)p.k + a + lane * 16, ld16(kn + lane * 16));
-        st16((uint8_t*)p.v + a + lane * 16, ld16(vn + lane * 16));
-    }
+    constexpr bool kStoreAfter = vec_waves_per_simd<T, D, GT>() == 2;
+    auto store_new_row = [&]() {
+        if (own_new && id_ok(pid) && lane < D * EB / 16) {
+            const int64_t a = tok_addr(pblk, pid, ptt);
+            st16((uint8_t*)p.k + a + lane * 16, ld16(kn + lane * 16));
+            st16((uint8_t*)p.v + a + lane * 16, ld16(vn + lane * 16));
+        }
+    };
+    if constexpr (!kStoreAfter) store_new_row();
 
     auto load = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
         const int32_t blk = first + kWaves * i;
@@ -517,6 +529,8 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
             }
         }
     }
+
+    if constexpr (kStoreAfter) store_new_row();
 
     // ---- merge lanes, then waves, through LDS ----
     // acc and lv: fold the V-layout token groups down to VR groups, park them
