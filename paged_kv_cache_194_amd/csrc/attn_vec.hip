@@ -627,36 +627,54 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     merge_splits<T, D, GT>(p, g, row, slot0, S);
 }
 
-// Zero the output rows that no unit covers: one lane per row.  The unit index
-// of the scan is the same in every lane, so the unit table is read with
-// broadcast (scalar) loads; each wave then clears its uncovered rows together,
-// 16 bytes per lane.
+// Zero the output rows that no unit covers.  A work group takes kZeroRows
+// rows: wave 0 reads the row ranges of 64 units per vector load and marks each
+// of its rows covered with one ballot per row, then the whole work group
+// clears the uncovered rows, 16 bytes per lane and store.
+constexpr int kZeroRows = 16;
+
 __global__ __launch_bounds__(256) void zero_uncovered_kernel(AttnParams p, int32_t row_bytes) {
-    const int lane = lane_id();
-    const int32_t r = blockIdx.x * 256 + threadIdx.x;
-    bool covered = r >= p.total_q;                  // past the end: nothing to write
-    for (int32_t u = 0; u < p.num_units; ++u) {
-        int32_t q0, L;
-        if (p.mode == kColumn) {
-            q0 = p.seq_info[4 * (int64_t)u];
-            L = p.seq_info[4 * (int64_t)u + 1];
-        } else if (p.mode == kPagedVarlen) {
-            q0 = p.cu_seqlens_q[u];
-            L = p.cu_seqlens_q[u + 1] - q0;
-        } else {
-            q0 = u;
-            L = 1;
+    __shared__ uint32_t sTodo;
+    const int32_t r0 = blockIdx.x * kZeroRows;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        uint32_t cov = 0;                           // bit i: row r0 + i is covered
+        for (int32_t ub = 0; ub < p.num_units; ub += 64) {
+            const int32_t u = ub + lane;
+            int32_t q0 = 0, L = 0;
+            if (u < p.num_units) {
+                if (p.mode == kColumn) {
+                    q0 = p.seq_info[4 * (int64_t)u];
+                    L = p.seq_info[4 * (int64_t)u + 1];
+                } else if (p.mode == kPagedVarlen) {
+                    q0 = p.cu_seqlens_q[u];
+                    L = p.cu_seqlens_q[u + 1] - q0;
+                } else {
+                    q0 = u;
+                    L = 1;
+                }
+                if (L > p.max_seqlen_q) L = p.max_seqlen_q;
+            }
+#pragma unroll
+            for (int i = 0; i < kZeroRows; ++i) {
+                const int32_t r = r0 + i;
+                if (__ballot(r >= q0 && r - q0 < L) != 0) cov |= 1u << i;
+            }
         }
-        if (L > p.max_seqlen_q) L = p.max_seqlen_q;
-        covered |= (r >= q0) && (r - q0 < L);
+        if (lane == 0) {
+            const int32_t n = min(kZeroRows, p.total_q - r0);          // rows inside the output
+            const uint32_t inside = n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+            sTodo = ~cov & inside;
+        }
     }
-    uint64_t todo = __ballot(!covered);
-    const int32_t r0 = r - lane;                    // first row of this wave
-    while (todo != 0) {
-        const int i = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        uint8_t* o = (uint8_t*)p.out + (int64_t)(r0 + i) * row_bytes;
-        for (int32_t c = lane; c < row_bytes / 16; c += 64) st16(o + (int64_t)c * 16, u32x4{0u, 0u, 0u, 0u});
+    __syncthreads();
+    const uint32_t todo = sTodo;
+    if (todo == 0) return;
+    const int32_t chunks = row_bytes / 16;
+    for (int32_t i = threadIdx.x; i < kZeroRows * chunks; i += 256) {
+        const int32_t rr = i / chunks, c = i - rr * chunks;
+        if ((todo >> rr) & 1u)
+            st16((uint8_t*)p.out + (int64_t)(r0 + rr) * row_bytes + (int64_t)c * 16, u32x4{0u, 0u, 0u, 0u});
     }
 }
 
@@ -740,7 +758,7 @@ hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t h
                                  hipStream_t stream) {
     const int32_t row_bytes = p.q_heads * head_dim * (dtype == PKV_BF16 ? 2 : 4);
     if (p.total_q <= 0) return hipSuccess;
-    zero_uncovered_kernel<<<dim3((p.total_q + 255) / 256), dim3(256), 0, stream>>>(p, row_bytes);
+    zero_uncovered_kernel<<<dim3((p.total_q + kZeroRows - 1) / kZeroRows), dim3(256), 0, stream>>>(p, row_bytes);
     return hipGetLastError();
 }
 
