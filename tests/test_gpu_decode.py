@@ -151,6 +151,11 @@ CASES = [
     (128, 32, 8, torch.float32),
     (256, 16, 2, torch.float32),
     (64, 8, 1, torch.float32),
+    # K layouts of 8 and 16 lanes per token with 2..8 chunks per lane
+    (256, 4, 2, torch.float32),
+    (256, 8, 2, torch.float32),
+    (128, 64, 8, torch.float32),
+    (64, 16, 16, torch.bfloat16),
 ]
 
 
