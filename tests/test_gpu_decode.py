@@ -106,6 +106,37 @@ def test_fused_decode_append_writes_block_table_slot():
 # decode attention parity
 # ---------------------------------------------------------------------------
 
+def test_long_ranges_past_one_id_group_with_fused_append():
+    """A split of more than 256 blocks gives each of the 4 waves more than 64
+    blocks, so block ids are read again for each further group of 64: 8192 and
+    4500 keys in one or two splits, permuted tables, with the fused append, and
+    again with a window of 3000 keys."""
+    lengths = [8192, 4500, 100]
+    H, D, B = 8, 128, len(lengths)
+    inp = workloads.paged_inputs(seed=91, lengths=lengths, q_lens=[1] * B, q_heads=32, kv_heads=H,
+                                 head_dim=D, dtype=torch.bfloat16, num_blocks=1000, max_blocks=512,
+                                 device=DEV)
+    kn = workloads.randn((B, H, D), torch.bfloat16, 92, DEV)
+    vn = workloads.randn((B, H, D), torch.bfloat16, 93, DEV)
+    bt = inp.block_table.cpu().numpy()
+    used = inp.seqused_k.cpu().numpy()
+    slots = np.array([oracle.paged_slot(bt[b], int(used[b]) - 1) for b in range(B)])
+    k_ref, v_ref = oracle.kv_append(raw(inp.k_cache).reshape(-1, H, D), raw(inp.v_cache).reshape(-1, H, D),
+                                    raw(kn), raw(vn), slots)
+    for window in (0, 3000):
+        ref = oracle.paged_attention(raw(inp.q), k_ref, v_ref, bt, np.arange(B + 1), used, dtype="bf16",
+                                     scale=inp.scale, max_seqlen_k=inp.max_seqlen_k, window=window)
+        for splits in (1, 2):
+            out = torch.full_like(inp.q, float("nan"))
+            pkv.paged_decode_attn(out, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seqused_k,
+                                  max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale, window=window,
+                                  num_splits=splits, k_new=kn, v_new=vn)
+            torch.cuda.synchronize()
+            assert np.array_equal(raw(inp.k_cache).reshape(-1, H, D), k_ref)
+            assert np.array_equal(raw(inp.v_cache).reshape(-1, H, D), v_ref)
+            check_close(out, ref, "bf16", f"window={window} splits={splits}")
+
+
 def run_decode(inp, num_splits=0, out=None, **kw):
     out = torch.full_like(inp.q, float("nan")) if out is None else out
     pkv.paged_decode_attn(out, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seqused_k,
