@@ -5,8 +5,9 @@
 // sdpa_varlen's column store, window, zeroed rows and split-K): for the query
 // row of a unit and each q head h of kv head g, softmax(q_h . K^T * scale) V
 // over the unit's visible live keys, read through the block table or ring.
-// With k_new/v_new (paged decode) the same kernel first puts this step's K/V
-// at position E-1, as PagedDecodeCache.attend does before attending.
+// With k_new/v_new (paged decode) the same kernel also writes this step's K/V
+// to position E-1 and attends over it as part of the prefix, as
+// PagedDecodeCache.attend does (append, then attend).
 //
 // One kernel per call.  Work decomposition: one work group (4 waves) per
 // (split, kv head, unit).  The unit's visible keys, as whole 16-token blocks,
