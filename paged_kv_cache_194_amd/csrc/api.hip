@@ -76,19 +76,23 @@ int32_t device_cus() {
     return n;
 }
 
-// Vector path, at least 8 blocks (two per wave) per split.  Several units:
-// about 2048 work groups (four dispatch rounds at two per CU; the balanced
-// deal keeps them even; the 64-sequence batch measured 207 us against 214 us
-// at 1024).  One unit: one work group per CU -- a single short round in which
+// Vector path.  Several units: about 2048 work groups (four dispatch rounds
+// at two per CU; the balanced deal keeps them even; the 64-sequence batch
+// measured 207 us against 214 us at 1024), at least 8 blocks (two per wave)
+// per split.  One unit: one work group per CU -- a single short round in which
 // every split's work group is on the critical path, each wave with the same
 // number of blocks where the length allows (the 4096-key, 8-head decode step
-// measured 434 us at 32 splits, 448 us at 24, 456 us at 28, 504 us at 36).
+// measured 434 us at 32 splits, 448 us at 24, 456 us at 28, 504 us at 36) --
+// and at least 4 blocks (one per wave) per split: the 42-layer step at 1024
+// keys measured 336 us at 16 splits against 362 us at 8, at 2048 keys 369 us
+// at 32 against 383 us at 16.
 int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_splits) {
     if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
     const int64_t base = (int64_t)(units > 0 ? units : 1) * kv_heads;
     const int64_t blocks = ((int64_t)(keys > 0 ? keys : 1) + 15) / 16;
     const int64_t target = units <= 1 ? (int64_t)device_cus() : 2048;
-    return clamp_splits((target + base - 1) / base, blocks / 8 > 0 ? blocks / 8 : 1);
+    const int64_t per = units <= 1 ? 4 : 8;         // blocks per split at least
+    return clamp_splits((target + base - 1) / base, blocks / per > 0 ? blocks / per : 1);
 }
 
 // Plan of one attention call: which paths run, their split counts and the
