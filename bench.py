@@ -39,25 +39,33 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "decode attention KV GB/s (% of HBM peak) + µs/step at 4K ctx, 1×MI355X"
 
 
-def kernel_source_hash() -> str:
+# Sources that decide a workload's dominant kernel: the kernel's own file,
+# the shared device headers and the host plan that sets its launch.
+TRAFFIC_SOURCES = {
+    "decode_step_4k": ["attn_vec.hip", "device_util.h", "internal.h", "api.hip"],
+    "prefix_import_4k": ["prefix_copy.hip", "device_util.h", "internal.h", "api.hip"],
+}
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_194_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(TRAFFIC_SOURCES[workload]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, launches_per_unit: float = 1.0):
+def traffic_from_profiles(workload: str):
     """HBM bytes per launch from committed PMC summaries, if they were taken on
-    the current kernel sources; else None."""
+    the current sources of the workload's kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
     rec = data.get(workload)
-    if not rec or rec.get("kernel_source_sha") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
