@@ -328,10 +328,6 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     };
     auto id_ok = [&](int32_t id) { return !PAGED || (id >= 0 && id < p.num_blocks); };
 
-    // Every load of the block loop is issued unconditionally -- a block with
-    // no storage loads pool block 0 and is skipped when processed -- so the
-    // compiler's wait counts see the same loads on every path and wait only
-    // for the block being processed, never for the one in flight behind it.
     // Fused append.  Position E-1 sits in the last live block, which is the
     // last block of the one wave that owns it.  Inside the loop, the lanes of
     // that wave that would read the row from the cache read it from k_new /
@@ -354,6 +350,10 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     };
     if constexpr (!kStoreAfter) store_new_row();
 
+    // Every load of the block loop is issued unconditionally -- a block with
+    // no storage loads pool block 0 and is skipped when processed -- so the
+    // compiler's wait counts see the same loads on every path and wait only
+    // for the block being processed, never for the one in flight behind it.
     auto load = [&](int i, int32_t id, u32x4 (&kr)[KNI][KCH], u32x4 (&vr)[VNI]) {
         const int32_t blk = first + kWaves * i;
         const int32_t idc = id_ok(id) ? id : 0;
