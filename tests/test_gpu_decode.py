@@ -106,6 +106,52 @@ def test_fused_decode_append_writes_block_table_slot():
 # decode attention parity
 # ---------------------------------------------------------------------------
 
+FUSED_ONE_WAVE = [
+    # (head_dim, q_heads, kv_heads, dtype): shapes held to one wave per SIMD,
+    # whose fused append stores the new row before the block loop
+    (256, 64, 8, torch.bfloat16),
+    (128, 64, 8, torch.bfloat16),
+    (128, 16, 4, torch.float32),
+]
+
+
+@pytest.mark.parametrize("D,hq,hkv,dtype", FUSED_ONE_WAVE,
+                         ids=[f"D{c[0]}-{c[1]}x{c[2]}-{str(c[3])[6:]}" for c in FUSED_ONE_WAVE])
+def test_fused_append_one_wave_shapes(D, hq, hkv, dtype):
+    lengths = [1, 16, 17, 300, 1000, 2049]
+    B = len(lengths)
+    inp = workloads.paged_inputs(seed=300 + D + hq, lengths=lengths, q_lens=[1] * B, q_heads=hq, kv_heads=hkv,
+                                 head_dim=D, dtype=dtype, num_blocks=400, max_blocks=160, device=DEV)
+    kn = workloads.randn((B, hkv, D), dtype, 301 + D, DEV)
+    vn = workloads.randn((B, hkv, D), dtype, 302 + D, DEV)
+    bt = inp.block_table.cpu().numpy()
+    used = inp.seqused_k.cpu().numpy()
+    slots = np.array([oracle.paged_slot(bt[b], int(used[b]) - 1) for b in range(B)])
+
+    def cache_bits(t):      # bit patterns: the unused pool blocks hold NaN
+        a = raw(t).reshape(-1, hkv, D)
+        return a.view(np.uint32) if a.dtype == np.float32 else a
+
+    def row_bits(t):
+        a = raw(t)
+        return a.view(np.uint32) if a.dtype == np.float32 else a
+
+    k_ref, v_ref = oracle.kv_append(cache_bits(inp.k_cache), cache_bits(inp.v_cache), row_bits(kn), row_bits(vn),
+                                    slots)
+    as_vals = (lambda a: a.view(np.float32)) if dtype == torch.float32 else (lambda a: a)
+    ref = oracle.paged_attention(raw(inp.q), as_vals(k_ref), as_vals(v_ref), bt, np.arange(B + 1), used,
+                                 dtype=dname(inp.q), scale=inp.scale, max_seqlen_k=inp.max_seqlen_k)
+    for splits in (1, 3, 0):
+        out = torch.full_like(inp.q, float("nan"))
+        pkv.paged_decode_attn(out, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seqused_k,
+                              max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale, num_splits=splits,
+                              k_new=kn, v_new=vn)
+        torch.cuda.synchronize()
+        assert np.array_equal(cache_bits(inp.k_cache), k_ref)
+        assert np.array_equal(cache_bits(inp.v_cache), v_ref)
+        check_close(out, ref, dname(inp.q), f"splits={splits}")
+
+
 def test_long_ranges_past_one_id_group_with_fused_append():
     """A split of more than 256 blocks gives each of the 4 waves more than 64
     blocks, so block ids are read again for each further group of 64: 8192 and
