@@ -115,6 +115,12 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
     pl.vec = group <= kVecMaxGroup;
     pl.mfma = max_seqlen_q > 1 || group > kVecMaxGroup;
     pl.splits = pick_splits(units, kv_heads, keys, num_splits);
+    // With multi-row units in the call the vector path serves only part of
+    // the units (the single-row ones, or none: which, only the device knows),
+    // so its library split count is capped at 4 (column-store step 396 us
+    // against 410 us at the uncapped 8; draft verify, no single-row unit,
+    // 442 us against 446 us).
+    if (num_splits == 0 && max_seqlen_q > 1 && pl.splits > 4) pl.splits = 4;
     pl.gt = pkv::vec_group_rows(group);
     if (pl.vec && pl.splits > 1) {
         pl.vec_ticket = pkv::ticket_bytes(U, kv_heads);
