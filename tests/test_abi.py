@@ -187,3 +187,26 @@ def test_split_choice_is_static_and_bounded():
     assert pkv.attn_num_splits(1, 1, 4096, 32, 8, 128, 16) == 16
     assert pkv.attn_num_splits(1, 1, 16, 32, 8, 128, 0) == 1
     assert pkv.attn_workspace_bytes(1, 1, 4096, 32, 8, 128, 1) == 0
+
+
+def test_split_choice_rules():
+    """The library's own split counts (num_splits = 0).  One sequence: one work
+    group per compute unit over its kv heads, at least 4 blocks (one per wave)
+    per split.  Several sequences: about 2048 work groups, at least 8 blocks per
+    split.  A call that holds multi-row units caps the vector path at 4."""
+    import torch
+    if torch.cuda.is_available():
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+    else:
+        cus = 256                        # the library's value when no device answers
+    one = lambda keys, hkv=8: pkv.attn_num_splits(1, 1, keys, 4 * hkv, hkv, 128, 0)
+    assert one(4096) == min(cus // 8, 4096 // 16 // 4)
+    assert one(1024) == min(cus // 8, 1024 // 16 // 4)
+    assert one(512) == min(cus // 8, 512 // 16 // 4)
+    assert one(64) == 1
+    assert one(8192, hkv=2) == min(cus // 2, 8192 // 16 // 4)
+    assert pkv.attn_num_splits(64, 1, 8192, 32, 8, 128, 0) == 4           # 2048 / (64 * 8)
+    assert pkv.attn_num_splits(4, 1, 65536, 64, 8, 256, 0) == 64           # 2048 / (4 * 8)
+    assert pkv.attn_num_splits(4, 16, 65536, 64, 8, 256, 0) == 4           # multi-row units: capped
+    assert pkv.attn_num_splits(32, 512, 16384, 32, 8, 128, 0) == 4
+    assert pkv.attn_num_splits(32, 512, 16384, 32, 8, 128, 6) == 6         # an explicit count is kept
