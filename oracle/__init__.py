@@ -40,6 +40,12 @@ support in the design notes):
   column ``kv_end`` below 0 counts as 0;
 * a live key whose block-table entry lies outside ``[0, num_blocks)``, or a
   segment whose column lies outside ``[0, cols)``, contributes no keys;
+* a non-finite V value in a live key that one row of a unit sees and another
+  row of the same unit does not (causal, window or padding rule) leaves the
+  output of the row that does not see it unspecified: a dense masked product
+  multiplies it by a zero weight.  The oracle computes that row from its
+  visible keys and, when asked, reports it in an ``unspecified`` mask
+  ``[total_q, Hq]`` that comparisons skip;
 * query rows of a unit past ``max_seqlen_q`` are treated as uncovered (0);
 * ``kv_append`` skips slots outside ``[0, num_slots)`` and copies raw bits;
 * prefix import takes the same rule; prefix export writes zero bits for a
@@ -169,6 +175,31 @@ def visible_range(E: int, L: int, i: int, causal: bool, window: int,
 # --------------------------------------------------------------------------
 
 
+def hidden_nonfinite(vals: np.ndarray, key_ok: np.ndarray, E: int, L: int, causal: bool,
+                     window: int, kv_start: int = 0) -> np.ndarray:
+    """bool [L, Hkv]: row ``i`` and kv head ``g`` have a live key with storage
+    whose V row (head ``g``) holds a non-finite value, that row ``i`` does not
+    see while some other row of the unit does.  Such a row's output is
+    unspecified (see the module docstring)."""
+    Hkv = vals.shape[1] if vals.ndim == 3 else 0
+    flags = np.zeros((L, Hkv), dtype=bool)
+    if L == 0 or E <= 0:
+        return flags
+    ranges = [visible_range(E, L, i, causal, window, kv_start) for i in range(L)]
+    seen = np.zeros(E, dtype=bool)
+    for lo, hi in ranges:
+        seen[lo:hi] = True
+    seen &= np.asarray(key_ok, dtype=bool)
+    bad = seen[:, None] & ~np.isfinite(vals).all(axis=2)          # [E, Hkv]
+    if not bad.any():
+        return flags
+    for i, (lo, hi) in enumerate(ranges):
+        hidden = np.ones(E, dtype=bool)
+        hidden[lo:hi] = False
+        flags[i] = (bad & hidden[:, None]).any(axis=0)
+    return flags
+
+
 def attend_unit(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, key_ok: np.ndarray,
                 E: int, scale: float, causal: bool, window: int,
                 chunk: int = 64, kv_start: int = 0) -> np.ndarray:
@@ -250,7 +281,7 @@ def _attend_chunks(q, keys, vals, key_ok, ranges, scale, G, Hkv, D, L, chunk, ou
 def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *,
                     dtype: str, scale: float, causal: bool = False, window: int = 0,
                     max_seqlen_q: int | None = None, max_seqlen_k: int | None = None,
-                    seqs=None, kv_start=None) -> np.ndarray:
+                    seqs=None, kv_start=None, with_unspecified: bool = False):
     """Oracle for varlen attention over a paged cache.
 
     q        raw [total_q, Hq, D]          (bits for bf16, float32 for f32)
@@ -259,7 +290,8 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *
     seqused_k int [num_seqs].  ``seqs`` restricts the work to some sequences
     (the other rows are left 0, as uncovered rows are).  ``kv_start`` int
     [num_seqs] or None: each sequence's left-padding bound.
-    Returns float64 [total_q, Hq, D].
+    Returns float64 [total_q, Hq, D]; with ``with_unspecified`` also the bool
+    mask [total_q, Hq] of outputs the module docstring leaves unspecified.
     """
     q = np.asarray(q)
     total_q, Hq, D = q.shape
@@ -275,6 +307,7 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *
     if max_seqlen_k is not None:
         cap = min(cap, int(max_seqlen_k))
     out = np.zeros((total_q, Hq, D), dtype=np.float64)
+    unspec = np.zeros((total_q, Hq), dtype=bool)
     for b in (range(num_seqs) if seqs is None else seqs):
         start, stop = int(cu[b]), int(cu[b + 1])
         L = stop - start
@@ -289,11 +322,15 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *
         qq = to_f64(q[start:stop], dtype)
         ks = 0 if kv_start is None else int(kv_start[b])
         res = attend_unit(qq, keys, vals, ok, E, scale, causal, window, kv_start=ks)
+        flags = (hidden_nonfinite(vals, ok, E, L, causal, window, ks) if with_unspecified
+                 else np.zeros((L, keys.shape[1]), dtype=bool))
+        G = Hq // keys.shape[1]
         for i in range(n_rows):
             r = start + i
             if 0 <= r < total_q:
                 out[r] = res[i]
-    return out
+                unspec[r] = np.repeat(flags[i], G)
+    return (out, unspec) if with_unspecified else out
 
 
 # --------------------------------------------------------------------------
@@ -303,11 +340,12 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, *
 
 def column_attention(q, k_store, v_store, seq_info, *, dtype: str, scale: float,
                      causal: bool, window: int, max_seqlen_q: int | None = None,
-                     segments=None, kv_start=None) -> np.ndarray:
+                     segments=None, kv_start=None, with_unspecified: bool = False):
     """Oracle for ``sdpa_varlen`` over a column (ring) store.  Key ``j`` of the
     segment's column sits in store row ``j % rows``.  ``kv_start`` int
     [num_segments] or None: each segment's left-padding bound.  Returns
-    float64 [total_q, Hq, D] with uncovered rows 0."""
+    float64 [total_q, Hq, D] with uncovered rows 0; with ``with_unspecified``
+    also the bool mask [total_q, Hq] of unspecified outputs."""
     q = np.asarray(q)
     total_q, Hq, D = q.shape
     ks = np.asarray(k_store)
@@ -315,6 +353,7 @@ def column_attention(q, k_store, v_store, seq_info, *, dtype: str, scale: float,
     rows, cols = ks.shape[0], ks.shape[1]
     info = np.asarray(seq_info).astype(np.int64)
     out = np.zeros((total_q, Hq, D), dtype=np.float64)
+    unspec = np.zeros((total_q, Hq), dtype=bool)
     for s in (range(info.shape[0]) if segments is None else segments):
         q_start, L, col, E = (int(x) for x in info[s])
         if L <= 0:
@@ -342,11 +381,15 @@ def column_attention(q, k_store, v_store, seq_info, *, dtype: str, scale: float,
         if hi_r > lo_r:
             qq[lo_r - q_start:hi_r - q_start] = to_f64(q[lo_r:hi_r], dtype)
         res = attend_unit(qq, keys, vals, ok, E, scale, causal, window, kv_start=pad)
+        flags = (hidden_nonfinite(vals, ok, E, L, causal, window, pad) if with_unspecified
+                 else np.zeros((L, ks.shape[2]), dtype=bool))
+        G = Hq // ks.shape[2]
         for i in range(n_rows):
             r = q_start + i
             if 0 <= r < total_q:
                 out[r] = res[i]
-    return out
+                unspec[r] = np.repeat(flags[i], G)
+    return (out, unspec) if with_unspecified else out
 
 
 # --------------------------------------------------------------------------
@@ -405,13 +448,30 @@ def prefix_export(k_flat: np.ndarray, v_flat: np.ndarray, block_table: np.ndarra
 # --------------------------------------------------------------------------
 
 
-def compare(got: np.ndarray, ref: np.ndarray) -> dict:
-    """max |got - ref| and RMS |got - ref| / RMS |ref| over finite references."""
+def compare(got: np.ndarray, ref: np.ndarray, skip=None) -> dict:
+    """Element-wise comparison of an output with the oracle's.
+
+    ``max_abs``: max |got - ref| over the elements where ``ref`` is finite;
+    ``rms_rel``: RMS |got - ref| / RMS |ref| over the same elements;
+    ``finite``: every ``got`` element is finite where ``ref`` is;
+    ``nan_match``: ``got`` is NaN exactly where ``ref`` is NaN (a NaN that
+    reaches a row through a key the row sees must show up, and only there).
+    ``skip`` (bool, broadcastable to the leading axes of ``got``) leaves
+    unspecified outputs out of every figure.
+    """
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    d = np.abs(got - ref)
-    rms_ref = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    keep = np.ones(got.shape, dtype=bool)
+    if skip is not None:
+        sk = np.asarray(skip, dtype=bool)
+        sk = sk.reshape(sk.shape + (1,) * (got.ndim - sk.ndim))
+        keep &= ~np.broadcast_to(sk, got.shape)
+    fin = keep & np.isfinite(ref)
+    d = np.abs(got - ref)[fin]
+    r = ref[fin]
+    rms_ref = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     rms_d = float(np.sqrt(np.mean(d * d))) if d.size else 0.0
     return {"max_abs": float(d.max()) if d.size else 0.0,
             "rms_rel": rms_d / rms_ref if rms_ref > 0 else rms_d,
-            "finite": bool(np.isfinite(got).all())}
+            "finite": bool(np.isfinite(got[fin]).all()),
+            "nan_match": bool(np.array_equal(np.isnan(got) & keep, np.isnan(ref) & keep))}

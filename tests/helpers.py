@@ -28,9 +28,13 @@ def bits(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-def check_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "") -> dict:
-    err = oracle.compare(got.detach().float().cpu().numpy(), ref)
+def check_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "", skip=None) -> dict:
+    """Every output element against the oracle: NaN exactly where the oracle
+    has NaN, finite elsewhere, max |err| and RMS relative error within the
+    dtype's bound.  ``skip`` [rows, heads] leaves unspecified outputs out."""
+    err = oracle.compare(got.detach().float().cpu().numpy(), ref, skip=skip)
     assert err["finite"], f"{what}: non-finite output"
+    assert err["nan_match"], f"{what}: NaN pattern differs from the oracle's"
     assert err["max_abs"] <= TOL[dtype], f"{what}: max |err| {err['max_abs']:.3e} > {TOL[dtype]}"
     assert err["rms_rel"] <= RMS_TOL[dtype], f"{what}: rms rel err {err['rms_rel']:.3e}"
     return err

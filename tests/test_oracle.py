@@ -75,8 +75,9 @@ def place_ring(store, col, logical):
 # Pure-Python brute force (the definition with nested loops and math.exp).
 # ---------------------------------------------------------------------------
 
-def brute_unit(q, K, V, E, scale, causal, window):
-    """q [L][Hq][D], K/V [E][Hkv][D] logical float lists -> out [L][Hq][D]."""
+def brute_unit(q, K, V, E, scale, causal, window, ok=None):
+    """q [L][Hq][D], K/V [E][Hkv][D] logical float lists -> out [L][Hq][D].
+    ``ok[j]`` False: key j has no storage and is left out of every row."""
     L, Hq, D = len(q), len(q[0]), len(q[0][0])
     Hkv = len(K[0]) if E else 1
     G = Hq // Hkv
@@ -88,6 +89,8 @@ def brute_unit(q, K, V, E, scale, causal, window):
             if causal and j > p:
                 continue
             if window > 0 and j < p - window + 1:
+                continue
+            if ok is not None and not ok[j]:
                 continue
             vis.append(j)
         if not vis:
@@ -167,6 +170,10 @@ def pin_golden_slots():
     for n, s in fx["decode_append"]["cases"]:
         ident = np.arange((n + 15) // 16 + 1)
         assert int(oracle.paged_slots_for(ident[None, :], [0], [n - 1])[0]) == s
+    r = fx["ring_unwritten"]
+    pos, col, want = zip(*r["cases"])
+    got = oracle.ring_slots_for(list(pos), list(col), r["rows"], r["cols"])
+    assert got.tolist() == list(want)
 
 
 def _golden_column(case, causal, window):
@@ -620,6 +627,124 @@ def pin_left_padding_is_translation():
             assert np.array_equal(z, none)
 
 
+def _brute_rows(q, K, V, E, scale, causal, window, ok=None):
+    return np.array(brute_unit(q.tolist(), K.tolist(), V.tolist(), E, scale, causal, window, ok))
+
+
+def pin_multichunk_rows(seed=13):
+    """Units of up to 130 rows, taken 1, 3, 7 or 64 rows at a time by the
+    oracle, against the brute force: every row, across chunk edges."""
+    rng = np.random.default_rng(seed)
+    for L, E, causal, window, chunk in ((130, 150, True, 0, 64), (130, 140, True, 9, 7),
+                                        (67, 67, False, 0, 3), (65, 90, True, 40, 64),
+                                        (20, 31, False, 5, 1), (129, 129, True, 0, 64)):
+        Hq, Hkv, D = 2, 1, 3
+        q = rng.standard_normal((L, Hq, D))
+        K = rng.standard_normal((E, Hkv, D))
+        V = rng.standard_normal((E, Hkv, D))
+        want = _brute_rows(q, K, V, E, 0.7, causal, window)
+        got = oracle.attend_unit(q, K, V, np.ones(E, bool), E, 0.7, causal, window, chunk=chunk)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12, err_msg=f"L={L} chunk={chunk}")
+
+
+def pin_hidden_nonfinite(seed=14):
+    """A NaN (or Inf) in a live key that some rows cannot see.  The oracle
+    computes each row from the keys it sees (brute force selects exactly
+    those): rows that cannot see it come out finite and equal to the brute
+    force, a row that sees a NaN V comes out NaN.  The unspecified mask flags
+    exactly the rows that cannot see a non-finite V another row sees, for the
+    kv head that holds it; a non-finite key no row sees flags nothing."""
+    rng = np.random.default_rng(seed)
+    L, E, Hq, Hkv, D = 6, 20, 4, 2, 3
+    q = rng.standard_normal((L, Hq, D))
+    for what, bad_key, bad_head, causal, window, val in (
+            ("V", E - 1, 1, True, 0, np.nan), ("K", E - 2, 0, True, 0, np.nan),
+            ("V", E - 3, 0, True, 0, np.inf), ("V", 0, 1, True, 8, np.nan)):
+        K = rng.standard_normal((E, Hkv, D))
+        V = rng.standard_normal((E, Hkv, D))
+        (V if what == "V" else K)[bad_key, bad_head, 1] = val
+        want = _brute_rows(q, K, V, E, 0.5, causal, window)
+        got = oracle.attend_unit(q, K, V, np.ones(E, bool), E, 0.5, causal, window)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12, equal_nan=True)
+        flags = oracle.hidden_nonfinite(V, np.ones(E, bool), E, L, causal, window)
+        expect = np.zeros((L, Hkv), bool)
+        seen_by = [oracle.visible_range(E, L, i, causal, window) for i in range(L)]
+        some_row_sees = any(lo <= bad_key < hi for lo, hi in seen_by)
+        if what == "V" and some_row_sees:
+            for i, (lo, hi) in enumerate(seen_by):
+                expect[i, bad_head] = not (lo <= bad_key < hi)
+        assert np.array_equal(flags, expect), (what, bad_key, flags, expect)
+        for i, (lo, hi) in enumerate(seen_by):
+            g = slice(bad_head * (Hq // Hkv), (bad_head + 1) * (Hq // Hkv))
+            sees = lo <= bad_key < hi
+            assert np.isnan(got[i, g]).any() == (sees and np.isnan(val) or (sees and what == "K")), (what, i)
+    # through the paged entry point: the mask lands on the unit's rows and the kv head's q heads
+    K = rng.standard_normal((32, 1, Hkv, D)).astype(np.float32)
+    V = rng.standard_normal((32, 1, Hkv, D)).astype(np.float32)
+    pool_k = np.full((2, 16, Hkv, D), 7.0, np.float32)
+    pool_v = np.full((2, 16, Hkv, D), 7.0, np.float32)
+    pool_k.reshape(32, Hkv, D)[:E] = K[:E, 0]
+    pool_v.reshape(32, Hkv, D)[:E] = V[:E, 0]
+    pool_v.reshape(32, Hkv, D)[E - 1, 1, 0] = np.nan
+    qq = rng.standard_normal((L + 1, Hq, D)).astype(np.float32)
+    out, unspec = oracle.paged_attention(qq, pool_k, pool_v, np.array([[0, 1]]), np.array([1, L + 1]),
+                                         np.array([E]), dtype="f32", scale=0.5, causal=True,
+                                         with_unspecified=True)
+    assert unspec.shape == (L + 1, Hq)
+    assert not unspec[0].any() and not unspec[L].any()
+    assert unspec[1:L, 2:].all() and not unspec[1:L, :2].any()
+    assert np.isnan(out[L, 2:, 0]).all() and np.isfinite(out[:L]).all()
+
+
+def pin_compare_known_answer():
+    """compare() on values worked by hand: errors over finite references only,
+    NaN placement, the skip mask."""
+    got = np.array([1.0, 2.0, np.nan, 4.0])
+    ref = np.array([1.0, 2.5, np.nan, 3.0])
+    c = oracle.compare(got, ref)
+    # |d| over the finite references = (0, 0.5, 1); RMS ratio sqrt(1.25 / 16.25) = sqrt(1/13)
+    assert c["max_abs"] == 1.0 and abs(c["rms_rel"] - (1 / 13) ** 0.5) < 1e-15
+    assert c["finite"] and c["nan_match"]
+    c = oracle.compare(np.array([1.0, np.nan, 3.0]), np.array([1.0, 2.0, 3.0]))
+    assert not c["finite"] and not c["nan_match"] and np.isnan(c["max_abs"])
+    c = oracle.compare(np.array([1.0, 2.0, 3.0]), np.array([1.0, np.nan, 3.0]))
+    assert c["finite"] and not c["nan_match"] and c["max_abs"] == 0.0
+    g2 = np.array([[[0.0, 9.0]], [[np.nan, 1.0]]])      # [rows, heads, d]
+    r2 = np.array([[[0.0, 1.0]], [[5.0, 1.0]]])
+    c = oracle.compare(g2, r2, skip=np.array([[False], [True]]))
+    assert c["max_abs"] == 8.0 and c["finite"] and c["nan_match"]
+    c = oracle.compare(g2, r2, skip=np.array([[True], [True]]))
+    assert c["max_abs"] == 0.0 and c["rms_rel"] == 0.0
+
+
+def pin_storage_missing_in_live_range(seed=15):
+    """Block-table entries outside the pool inside the live range: those 16
+    keys drop out of every row (brute force with the keys left out), and a
+    row whose visible keys all lack storage is 0."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D, E, L = 2, 1, 4, 60, 12
+    K = rng.standard_normal((E, Hkv, D)).astype(np.float32)
+    V = rng.standard_normal((E, Hkv, D)).astype(np.float32)
+    table = np.array([[3, -1, 0, 0x7FFFFFFF]])           # keys 16..31 and 48..59 without storage
+    table[0, 2] = 1
+    pool_k = np.full((4, 16, Hkv, D), np.nan, np.float32)
+    pool_v = np.full((4, 16, Hkv, D), np.nan, np.float32)
+    pool_k[3, :] = K[:16]
+    pool_v[3, :] = V[:16]
+    pool_k[1, :] = K[32:48]
+    pool_v[1, :] = V[32:48]
+    ok = np.array([(j < 16) or (32 <= j < 48) for j in range(E)])
+    q = rng.standard_normal((L, Hq, D)).astype(np.float32)
+    for causal, window in ((True, 0), (False, 0), (True, 10)):
+        got = oracle.paged_attention(q, pool_k, pool_v, table, np.array([0, L]), np.array([E]), dtype="f32",
+                                     scale=0.3, causal=causal, window=window)
+        want = _brute_rows(q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), E, 0.3,
+                           causal, window, ok)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+        if window == 10:           # the last rows see keys 50..59 only: all without storage
+            assert np.array_equal(got[-1], np.zeros((Hq, D)))
+
+
 ALL_PINS = [
     pin_bf16_decode,
     pin_golden_causal_rule, pin_golden_slots, pin_golden_closed_forms, pin_window_span,
@@ -629,6 +754,8 @@ ALL_PINS = [
     pin_closed_form_means, pin_kv_append_bits,
     pin_golden_prefix_copy, pin_prefix_identity_is_transpose, pin_prefix_roundtrip_permuted,
     pin_golden_padded_mask, pin_left_padding_is_translation,
+    pin_multichunk_rows, pin_hidden_nonfinite, pin_compare_known_answer,
+    pin_storage_missing_in_live_range,
 ]
 
 
@@ -739,6 +866,65 @@ def _padding_off_by_one(E, L, i, causal, window, kv_start=0):
     return _real_visible(E, L, i, causal, window, kv_start + 1 if kv_start > 0 else 0)
 
 
+_real_chunks = oracle._attend_chunks
+
+
+def _chunk_drops_last_row(q, keys, vals, key_ok, ranges, scale, G, Hkv, D, L, chunk, out):
+    """Each chunk of rows stops one row short (an off-by-one at the chunk edge)."""
+    for c0 in range(0, L, chunk):
+        sub = [r if c0 <= i < min(L, c0 + chunk - 1) else (0, 0) for i, r in enumerate(ranges)]
+        _real_chunks(q, keys, vals, key_ok, sub, scale, G, Hkv, D, L, chunk, out)
+
+
+def _chunk_no_fallback(q, keys, vals, key_ok, ranges, scale, G, Hkv, D, L, chunk, out):
+    """Hidden non-finite keys not special-cased (0 * NaN leaks into rows)."""
+    with np.errstate(invalid="ignore"):
+        for c0 in range(0, L, chunk):
+            rows = [i for i in range(c0, min(L, c0 + chunk)) if ranges[i][1] > ranges[i][0]]
+            if not rows:
+                continue
+            lo_c = min(ranges[i][0] for i in rows)
+            hi_c = max(ranges[i][1] for i in rows)
+            j = np.arange(lo_c, hi_c)
+            mask = np.stack([(j >= ranges[i][0]) & (j < ranges[i][1]) for i in rows]) & key_ok[lo_c:hi_c][None, :]
+            for g in range(Hkv):
+                hs = slice(g * G, (g + 1) * G)
+                s = scale * np.einsum("rgd,kd->rgk", q[rows][:, hs, :], keys[lo_c:hi_c, g, :])
+                s = np.where(mask[:, None, :], s, -np.inf)
+                m = s.max(axis=2, keepdims=True)
+                w = np.exp(s - m)
+                out[rows, hs, :] = (w @ vals[lo_c:hi_c, g, :]) / w.sum(axis=2, keepdims=True)
+
+
+def _flags_never(vals, key_ok, E, L, causal, window, kv_start=0):
+    return np.zeros((L, vals.shape[1] if vals.ndim == 3 else 0), dtype=bool)
+
+
+_real_compare = oracle.compare
+
+
+def _compare_all_elements(got, ref, skip=None):
+    c = _real_compare(got, ref, skip)
+    d = np.abs(np.asarray(got, float) - np.asarray(ref, float))
+    c["max_abs"] = float(np.nanmax(d)) if d.size else 0.0
+    return c
+
+
+def _compare_ignores_nan(got, ref, skip=None):
+    c = _real_compare(got, ref, skip)
+    c["nan_match"] = True
+    return c
+
+
+def _ring_slots_no_skip(pos, col, rows, cols):
+    return np.array([(p % rows) * cols + c for p, c in zip(pos, col)], dtype=np.int64)
+
+
+def _storage_ignored(row, E, nb):
+    slots, ok = _real_gather(row, E, nb)
+    return slots, np.ones_like(ok)
+
+
 MUTANTS = [
     ("visible_range", _top_left_causal),
     ("visible_range", _window_off_by_one),
@@ -760,6 +946,13 @@ MUTANTS = [
     ("visible_range", _padding_ignored),
     ("visible_range", _pad_rows_see_nothing),
     ("visible_range", _padding_off_by_one),
+    ("_attend_chunks", _chunk_drops_last_row),
+    ("_attend_chunks", _chunk_no_fallback),
+    ("hidden_nonfinite", _flags_never),
+    ("compare", _compare_all_elements),
+    ("compare", _compare_ignores_nan),
+    ("ring_slots_for", _ring_slots_no_skip),
+    ("gather_slots_paged", _storage_ignored),
 ]
 
 
