@@ -47,9 +47,18 @@
  *      a live key whose block-table entry is outside [0, num_blocks), or a
  *      segment whose column is outside [0, cols), contributes no keys;
  *      a row with no visible key is 0, and so is every row of [0, total_q)
- *      that no unit covers (rows of a unit past max_seqlen_q count as uncovered);
+ *      that no unit covers (rows of a unit past max_seqlen_q count as uncovered,
+ *      so with max_seqlen_q = 1 each unit's row 0 alone is computed, at
+ *      position E - L);
  *      only the live keys a unit can see are read: storage past seqused_k and
- *      block-table entries past ceil(E / 16) are never dereferenced.
+ *      block-table entries past ceil(E / 16) are never dereferenced, and
+ *      values stored there (NaN included) never reach the output;
+ *      a non-finite value in a key a row sees makes that row non-finite; a
+ *      non-finite V value in a live key that another row of the same unit sees
+ *      but this row does not (causal, window or kv_start rule) leaves this
+ *      row's output unspecified (units of several rows multiply it by a zero
+ *      weight in a dense product, and 0 * NaN is NaN); rows of other units and
+ *      other kv heads are unaffected.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

@@ -96,7 +96,9 @@ int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_s
 }
 
 // Plan of one attention call: which paths run, their split counts and the
-// workspace layout (vector tickets | vector partials | mfma tickets | mfma partials).
+// workspace layout (vector tickets | mfma tickets | vector partials | mfma
+// partials).  The arrival counters come first, so their places depend on the
+// units, kv heads and row tiles only, not on the split counts.
 struct Plan {
     bool vec, mfma;
     int32_t splits;          // vector path
@@ -148,9 +150,12 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
         pl.tiles = 0;
         pl.msplits = 1;
     }
-    pl.ws_bytes = pl.vec_ticket + pl.vec_bytes + pl.mfma_ticket + pl.mfma_bytes;
+    pl.ws_bytes = pl.vec_ticket + pl.mfma_ticket + pl.vec_bytes + pl.mfma_bytes;
     return pl;
 }
+
+// Bytes at the start of the workspace that hold arrival counters.
+size_t plan_ticket_bytes(const Plan& pl) { return pl.vec_ticket + pl.mfma_ticket; }
 
 // Enqueue the attention kernels for a fully checked parameter block.
 pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, const Plan& pl,
@@ -160,10 +165,11 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
     p.ws_ticket = nullptr;
     p.ws_o = p.ws_ml = nullptr;
     p.vec_wgs = pkv::vec_slots(p.num_units, pl.splits);
+    char* partials = ws + plan_ticket_bytes(pl);
     if (pl.vec_bytes) {
         const size_t n = (size_t)p.vec_wgs * p.kv_heads * pl.gt;
         p.ws_ticket = (int32_t*)ws;
-        p.ws_o = (float*)(ws + pl.vec_ticket);
+        p.ws_o = (float*)partials;
         p.ws_ml = p.ws_o + n * head_dim;
     }
     p.mfma_tiles = pl.tiles;
@@ -171,10 +177,9 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
     p.mws_ticket = nullptr;
     p.mws_o = p.mws_ml = nullptr;
     if (pl.mfma_bytes) {
-        char* base = ws + pl.vec_ticket + pl.vec_bytes;
         const size_t n = (size_t)p.num_units * p.kv_heads * pl.tiles * pl.msplits * pl.bm;
-        p.mws_ticket = (int32_t*)base;
-        p.mws_o = (float*)(base + pl.mfma_ticket);
+        p.mws_ticket = (int32_t*)(ws + pl.vec_ticket);
+        p.mws_o = (float*)(partials + pl.vec_bytes);
         p.mws_ml = p.mws_o + n * head_dim;
     }
     if (p.num_units == 0 && p.total_q == 0) return ok();
@@ -308,15 +313,18 @@ int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seq
     return make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).splits;
 }
 
-pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
-                                 int32_t num_blocks, int32_t block_size, const int32_t* block_table,
-                                 int32_t max_blocks_per_seq, const int32_t* seqused_k,
-                                 int32_t num_seqs, int32_t max_seqlen_k, const void* k_new,
-                                 const void* v_new, int32_t q_heads, int32_t kv_heads,
-                                 int32_t head_dim, float softmax_scale, int32_t causal,
-                                 int32_t window, const int32_t* kv_start, int32_t num_splits,
-                                 void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-                                 void* stream) {
+}  // extern "C"
+
+namespace pkv {
+
+pkv_status decode_check(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* seqused_k, int32_t num_seqs,
+                        int32_t max_seqlen_k, const void* k_new, const void* v_new,
+                        int32_t q_heads, int32_t kv_heads, int32_t head_dim, float softmax_scale,
+                        int32_t num_splits, pkv_dtype dtype, size_t* ws_bytes, size_t* ticket_bytes) {
+    *ws_bytes = 0;
+    *ticket_bytes = 0;
     pkv_status s = check_heads(q_heads, kv_heads, head_dim, dtype);
     if (s != PKV_OK) return s;
     if (block_size != PKV_BLOCK_SIZE) return fail(PKV_EINVAL, "block_size %d: must be 16", block_size);
@@ -331,12 +339,39 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, 
         return fail(PKV_EUNSUPPORTED, "q_heads / kv_heads = %d > 8 needs bf16 (matrix-core path)", group);
     if (group > kVecMaxGroup && k_new)
         return fail(PKV_EUNSUPPORTED, "fused append with q_heads / kv_heads > 8: call pkv_kv_append first");
-    if (num_seqs == 0) return ok();
+    if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !seqused_k)
         return fail(PKV_EINVAL, "null pointer argument");
     const Plan pl = make_plan(num_seqs, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
-    if (workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !workspace))
-        return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.ws_bytes);
+    *ws_bytes = pl.ws_bytes;
+    *ticket_bytes = plan_ticket_bytes(pl);
+    return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* seqused_k,
+                                 int32_t num_seqs, int32_t max_seqlen_k, const void* k_new,
+                                 const void* v_new, int32_t q_heads, int32_t kv_heads,
+                                 int32_t head_dim, float softmax_scale, int32_t causal,
+                                 int32_t window, const int32_t* kv_start, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                 void* stream) {
+    size_t need = 0, tickets = 0;
+    pkv_status s = pkv::decode_check(out, q, k_cache, v_cache, num_blocks, block_size, block_table,
+                                     max_blocks_per_seq, seqused_k, num_seqs, max_seqlen_k, k_new, v_new,
+                                     q_heads, kv_heads, head_dim, softmax_scale, num_splits, dtype, &need,
+                                     &tickets);
+    if (s != PKV_OK) return s;
+    if (num_seqs == 0) return ok();
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const Plan pl = make_plan(num_seqs, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    const int32_t group = q_heads / kv_heads;
 
     const int64_t cap64 = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
     const int32_t kv_cap = (int32_t)(cap64 < max_seqlen_k ? cap64 : max_seqlen_k);

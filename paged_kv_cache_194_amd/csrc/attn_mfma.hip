@@ -324,9 +324,30 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     // block (c0 >> 4) + (r >> 4) at slot r & 15; a ring row is found from one
     // modulo per chunk.  A key not wanted, or without storage, reads the zero row.
     const int64_t blk_stride = 16 * tok_stride;
+    // Blocks without storage: bit KT*st + k is set when 16-key tile k of the
+    // chunk in stage st has a block-table entry outside the pool.  Those keys
+    // are staged from the zero row and must also be kept out of every row's
+    // softmax, like keys outside its range.  Wave-uniform; each stage's bits
+    // are set when its chunk is issued and read when it is computed.
+    static_assert(KT * NS <= 32, "storage mask bits");
+    uint32_t nostore = 0u;
     auto issue = [&](int32_t c, int st) __attribute__((always_inline)) {
         const int32_t c0 = c_base + c * BN;
         const bool chunk_ok = c < c_end;
+        if constexpr (PAGED) {
+            uint32_t bad = 0u;
+            if (chunk_ok) {
+#pragma unroll
+                for (int k = 0; k < KT; ++k) {
+                    int32_t w = (c0 >> 4) + k - id_base;
+                    w = w < 0 ? 0 : (w >= kIdWindow ? kIdWindow - 1 : w);
+                    const int32_t id = sIds[w];
+                    bad |= (id >= 0 && id < p.num_blocks) ? 0u : (1u << k);
+                }
+            }
+            const uint32_t field = ((1u << KT) - 1u) << (KT * st);
+            nostore = (nostore & ~field) | (bad << (KT * st));
+        }
         const uint32_t kdst = lds_addr(&sKV[st][0]), vdst = lds_addr(&sKV[st][CB]);
         int32_t ring0 = 0;
         if constexpr (!PAGED) ring0 = c0 % p.rows;
@@ -381,8 +402,9 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
         }
     };
 
-    auto compute = [&](int32_t c, const uint8_t* sKb, const uint8_t* sVb) __attribute__((always_inline)) {
+    auto compute = [&](int32_t c, int st_idx, const uint8_t* sKb, const uint8_t* sVb) __attribute__((always_inline)) {
         const int32_t c0 = c_base + c * BN;
+        const uint32_t bad = (nostore >> (KT * st_idx)) & ((1u << KT) - 1u);   // tiles without storage
         // A wave issues its two MFMA passes at raised priority and its softmax at
         // the normal one, so that on a SIMD shared with a wave of another phase
         // the matrix core is fed first and the VALU work fills the gaps (the
@@ -413,7 +435,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
             edge |= rows_ok[rt] && !(my_lo[rt] <= c0 && c0 + BN <= my_hi[rt]);
-        const bool masked = __ballot(edge) != 0;
+        const bool masked = __ballot(edge) != 0 || bad != 0u;
         uint32_t pk[RT][KT][2];                   // probabilities, bf16, 4 keys per tile
         float alpha[RT];
         bool moved = false;
@@ -428,7 +450,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int32_t j = c0 + kt * 16 + 4 * lq + e;
-                        const bool v = j >= my_lo[rt] && j < my_hi[rt];
+                        const bool v = j >= my_lo[rt] && j < my_hi[rt] && !((bad >> kt) & 1u);
                         vis |= (v ? 1u : 0u) << (kt * 4 + e);
                         cmax = v ? fmaxf(cmax, st[rt][kt][e]) : cmax;
                     }
@@ -519,7 +541,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             if (i + NS - 1 < n) ensure_ids(c_first + i + NS - 1);
             issue(c_first + i + NS - 1, (i + NS - 1) % NS);
             const int st = i % NS;
-            compute(c_first + i, &sKV[st][0], &sKV[st][CB]);
+            compute(c_first + i, st, &sKV[st][0], &sKV[st][CB]);
         }
         wait_vm<0>();                             // no load may land after the work group ends
     }

@@ -82,14 +82,21 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     }
 }
 
+// Whether the vector path computes unit ui: a unit of one query row, or the
+// first row of any unit when the call's static bound max_seqlen_q is 1 (the
+// matrix-core path takes the other multi-row units).
+__device__ __forceinline__ bool vec_takes(const AttnParams& p, const UnitInfo& ui) {
+    return ui.q_len == 1 || (ui.q_len > 1 && p.max_seqlen_q == 1);
+}
+
 // Live 16-key blocks of unit u for the vector path, or -1 when the unit is
-// not this path's (several query rows, or its row outside the output).
+// not this path's (see vec_takes, or its row outside the output).
 __device__ __forceinline__ int32_t vec_unit_blocks(const AttnParams& p, int32_t u) {
     const UnitInfo ui = load_unit(p, u);
-    if (ui.q_len != 1 || ui.q_start < 0 || ui.q_start >= p.total_q) return -1;
+    if (!vec_takes(p, ui) || ui.q_start < 0 || ui.q_start >= p.total_q) return -1;
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
-    const int32_t lo = single_row_lo(p, E, ui.pad);
-    const int32_t b_end = (E + 15) >> 4, b_first = lo >> 4;
+    const KeyRange kr = first_row_keys(p, E, ui.q_len, ui.pad);
+    const int32_t b_end = (kr.hi + 15) >> 4, b_first = kr.lo >> 4;
     return b_end > b_first ? b_end - b_first : 0;
 }
 
@@ -252,17 +259,18 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     }
 
     const UnitInfo ui = load_unit(p, u);
-    if (ui.q_len != 1) return;                      // other units are not this path's
+    if (!vec_takes(p, ui)) return;                  // other units are not this path's
     const int32_t row = ui.q_start;
     if (row < 0 || row >= p.total_q) return;
 
     const int32_t G = p.group;
     const int32_t Hkv = p.kv_heads;
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
-    // One query at position E-1: keys [lo, E) with the window's and the
-    // left-padding lower bounds.
-    const int32_t lo = single_row_lo(p, E, ui.pad);
-    const int32_t hi = E;
+    // One query row at position E - q_len: keys [lo, hi) with the causal,
+    // window and left-padding bounds.
+    const KeyRange krange = first_row_keys(p, E, ui.q_len, ui.pad);
+    const int32_t lo = krange.lo;
+    const int32_t hi = krange.hi;
     const int32_t b_end = (hi + 15) >> 4;
     const int32_t b_first = lo >> 4;
     const int32_t nblk = b_end > b_first ? b_end - b_first : 0;

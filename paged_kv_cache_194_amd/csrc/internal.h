@@ -91,15 +91,40 @@ __device__ __forceinline__ UnitInfo load_unit(const AttnParams& p, int32_t u) {
     return ui;
 }
 
-// First key of a unit's single query row (position E - 1): the window's bound
-// and the left-padding bound; a row before the padding bound (a pad query)
-// keeps only its own key (tiny-llm kv_cache.py, padded_causal_mask).
-__device__ __forceinline__ int32_t single_row_lo(const AttnParams& p, int32_t E, int32_t pad) {
-    const int32_t lo = (p.window > 0 && E - p.window > 0) ? E - p.window : 0;
-    if (pad <= 0) return lo;
-    if (E - 1 < pad) return E > 1 ? E - 1 : 0;
-    return lo > pad ? lo : pad;
+// Key range [lo, hi) of the first query row of a unit of L rows over E keys,
+// the row the vector path computes: the unit's only row, or row 0 when the
+// call's static bound max_seqlen_q is 1 (later rows are then uncovered).  The
+// row sits at position pos = E - L (tiny-llm kv_cache.py, causal_kwargs:
+// bottom-right alignment).  Causal: keys up to pos; window W: the W keys
+// ending at pos; left-padding bound pad > 0: no key before it, and a row
+// before it (a pad query) keeps only its own key (padded_causal_mask).
+struct KeyRange {
+    int32_t lo, hi;
+};
+__device__ __forceinline__ KeyRange first_row_keys(const AttnParams& p, int32_t E, int32_t L, int32_t pad) {
+    const int32_t pos = E - L;
+    KeyRange r;
+    if (pad > 0 && pos < pad) {
+        r.lo = pos > 0 ? pos : 0;
+        r.hi = pos + 1 < E ? pos + 1 : E;
+    } else {
+        r.hi = p.causal ? (pos + 1 < E ? pos + 1 : E) : E;
+        r.lo = (p.window > 0 && pos - p.window + 1 > 0) ? pos - p.window + 1 : 0;
+        if (pad > r.lo) r.lo = pad;
+    }
+    if (r.hi < r.lo) r.hi = r.lo;
+    return r;
 }
+
+// The host checks of pkv_paged_decode_attn, without enqueuing anything; on
+// PKV_OK also the workspace bytes the call needs and how many of them, at the
+// start, hold split-K arrival counters.
+pkv_status decode_check(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* seqused_k, int32_t num_seqs,
+                        int32_t max_seqlen_k, const void* k_new, const void* v_new,
+                        int32_t q_heads, int32_t kv_heads, int32_t head_dim, float softmax_scale,
+                        int32_t num_splits, pkv_dtype dtype, size_t* ws_bytes, size_t* ticket_bytes);
 
 // Text for pkv_last_error() on the calling thread.
 void set_error(const char* fmt, ...);

@@ -152,60 +152,140 @@ def test_mixed_column_segments_small():
         check_close(out, ref, "bf16", f"column splits={s}")
 
 
-def test_column_store_full_size_sampled():
-    """Store [8192, 32, 8, 128] bf16, 32 segments (24 decode + 8 chunked prefill of
-    64..512 rows) packed into 4096 rows, causal, window 4096, ring wrap; new tokens
-    appended first.  Checked: every uncovered row is 0, every covered row finite,
-    and a sample of segments (the longest prefill, 3 decode) against the oracle."""
-    inp = workloads.c4_column(device=DEV)
-    pkv.kv_append(inp.k_store, inp.v_store, inp.k_new, inp.v_new, ring_slots(inp))
-    out = torch.full_like(inp.q, float("nan"))
-    pkv.varlen_attn(out, inp.q, inp.k_store, inp.v_store, seq_info=inp.seq_info,
-                    max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=4096 + inp.max_seqlen_q - 1,
-                    softmax_scale=inp.scale, causal=True, window=4096)
-    torch.cuda.synchronize()
-    covered = torch.from_numpy(inp.new_pos.cpu().numpy() >= 0).to(DEV)
-    assert (out[~covered] == 0).all()
-    assert torch.isfinite(out[covered].float()).all()
+def _column_full_check(inp, out, q, what):
+    """Every segment's rows of every kv head against the oracle, one kv head
+    at a time (keeps the oracle's fp64 copies small)."""
     info = inp.seq_info.cpu().numpy()
-    pre = [s for s in range(len(info)) if info[s, 1] > 1]
-    dec = [s for s in range(len(info)) if info[s, 1] == 1]
-    pick = [max(pre, key=lambda s: info[s, 1])] + dec[:3]
-    # one kv head at a time keeps the oracle's fp64 copies small
-    G = 4
-    for g in (0, 5):
-        qg = inp.q[:, g * G:(g + 1) * G].contiguous()
+    G = inp.q_heads // inp.kv_heads
+    rows = np.concatenate([np.arange(r[0], r[0] + r[1]) for r in info])
+    for g in range(inp.kv_heads):
+        qg = q[:, g * G:(g + 1) * G].contiguous()
         ref = oracle.column_attention(raw(qg), raw(inp.k_store[:, :, g:g + 1]), raw(inp.v_store[:, :, g:g + 1]),
                                       info, dtype="bf16", scale=inp.scale, causal=True, window=4096,
-                                      segments=pick)
-        rows = np.concatenate([np.arange(info[s, 0], info[s, 0] + info[s, 1]) for s in pick])
-        check_close(out[rows, g * G:(g + 1) * G], ref[rows], "bf16", f"column head {g}")
+                                      max_seqlen_q=inp.max_seqlen_q)
+        check_close(out[rows, g * G:(g + 1) * G], ref[rows], "bf16", f"{what} kv head {g}")
 
 
-def test_long_context_draft_and_decode_sampled():
+def test_column_store_full_size():
+    """Store [8192, 32, 8, 128] bf16, 32 segments (24 decode + 8 chunked prefill of
+    64..512 rows) packed into 4096 rows, causal, window 4096, ring wrap; new tokens
+    appended first.  Every uncovered row is 0; every row of every segment and every
+    kv head against the oracle, with the library's split choice and with q scaled
+    by 4 (peaked)."""
+    inp = workloads.c4_column(device=DEV)
+    pkv.kv_append(inp.k_store, inp.v_store, inp.k_new, inp.v_new, ring_slots(inp))
+    covered = torch.from_numpy(inp.new_pos.cpu().numpy() >= 0).to(DEV)
+    q4 = (inp.q.float() * 4).to(torch.bfloat16)
+    for what, q in (("column store", inp.q), ("column store, peaked", q4)):
+        out = torch.full_like(q, float("nan"))
+        pkv.varlen_attn(out, q, inp.k_store, inp.v_store, seq_info=inp.seq_info,
+                        max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=4096 + inp.max_seqlen_q - 1,
+                        softmax_scale=inp.scale, causal=True, window=4096)
+        torch.cuda.synchronize()
+        assert (out[~covered] == 0).all(), what
+        _column_full_check(inp, out, q, what)
+
+
+def _paged_full_check(inp, out, q, what):
+    G = inp.q_heads // inp.kv_heads
+    bt = inp.block_table.cpu().numpy()
+    for g in range(inp.kv_heads):
+        qg = q[:, g * G:(g + 1) * G].contiguous()
+        ref = oracle.paged_attention(raw(qg), raw(inp.k_cache[:, :, g:g + 1]), raw(inp.v_cache[:, :, g:g + 1]),
+                                     bt, inp.cu_seqlens_q.cpu().numpy(), inp.seqused_k.cpu().numpy(),
+                                     dtype="bf16", scale=inp.scale, causal=inp.causal,
+                                     max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k)
+        check_close(out[:, g * G:(g + 1) * G], ref, "bf16", f"{what} kv head {g}")
+
+
+def test_long_context_draft_and_decode_full_size():
     """4 sequences at 32768/65536 keys, 64 q / 8 kv heads, D 256, random block
     tables: the 16-token draft blocks are appended, then verified non-causally;
-    then the single-token causal decode over the same keys with 16 splits."""
+    then the single-token causal decode over the same keys with 16 splits.  Every
+    row of every sequence and kv head against the oracle, plain and with q scaled
+    by 4 (peaked)."""
     draft = workloads.c5_long(device=DEV)
     pkv.kv_append(draft.k_cache, draft.v_cache, draft.k_new, draft.v_new, paged_slots(draft))
-    out = run_varlen_paged(draft)
-    assert torch.isfinite(out.float()).all()
     dec = workloads.c5_long(device=DEV, decode=True)
     dec.k_cache, dec.v_cache = draft.k_cache, draft.v_cache     # same keys, draft tokens included
-    out_d = torch.full_like(dec.q, float("nan"))
-    pkv.paged_decode_attn(out_d, dec.q, dec.k_cache, dec.v_cache, dec.block_table, dec.seqused_k,
-                          max_seqlen_k=dec.max_seqlen_k, softmax_scale=dec.scale, causal=True, num_splits=16)
-    torch.cuda.synchronize()
-    assert torch.isfinite(out_d.float()).all()
-    G = 8
-    bt = draft.block_table.cpu().numpy()
-    for g in (0, 7):
-        for which, inp, o in (("draft", draft, out), ("decode", dec, out_d)):
-            qg = inp.q[:, g * G:(g + 1) * G].contiguous()
-            ref = oracle.paged_attention(raw(qg), raw(inp.k_cache[:, :, g:g + 1]), raw(inp.v_cache[:, :, g:g + 1]),
-                                         bt, inp.cu_seqlens_q.cpu().numpy(), inp.seqused_k.cpu().numpy(),
-                                         dtype="bf16", scale=inp.scale, causal=inp.causal,
-                                         max_seqlen_k=inp.max_seqlen_k, seqs=[0, 1])
-            cu = inp.cu_seqlens_q.cpu().numpy()
-            rows = np.arange(cu[0], cu[2])
-            check_close(o[rows, g * G:(g + 1) * G], ref[rows], "bf16", f"{which} head {g}")
+    for scale_q in (1, 4):
+        qd = (draft.q.float() * scale_q).to(torch.bfloat16)
+        out = run_varlen_paged(draft, q=qd)
+        _paged_full_check(draft, out, qd, f"draft x{scale_q}")
+        qs = (dec.q.float() * scale_q).to(torch.bfloat16)
+        out_d = torch.full_like(qs, float("nan"))
+        pkv.paged_decode_attn(out_d, qs, dec.k_cache, dec.v_cache, dec.block_table, dec.seqused_k,
+                              max_seqlen_k=dec.max_seqlen_k, softmax_scale=dec.scale, causal=True,
+                              num_splits=16)
+        torch.cuda.synchronize()
+        _paged_full_check(dec, out_d, qs, f"decode x{scale_q}")
+
+
+def test_block_without_storage_inside_live_range():
+    """A block-table entry outside the pool inside a unit's live range: its 16
+    keys contribute nothing to any row (multi-row causal units on the matrix
+    cores, and a GQA group of 16 in paged_decode_attn)."""
+    inp = workloads.paged_inputs(seed=76, lengths=[100, 260, 64], q_lens=[20, 33, 16], q_heads=32,
+                                 kv_heads=8, head_dim=128, dtype=torch.bfloat16, num_blocks=40,
+                                 max_blocks=20, causal=True, device=DEV)
+    inp.block_table[0, 2] = -1                   # keys 32..47 of unit 0
+    inp.block_table[1, 15] = 1 << 30             # keys 240..255 of unit 1: seen by its last rows
+    inp.block_table[2, 0] = 40                   # keys 0..15 of unit 2 (= num_blocks)
+    ref = oracle_paged(inp)
+    for s in (0, 1, 3):
+        check_close(run_varlen_paged(inp, num_splits=s), ref, "bf16", f"multi-row splits={s}")
+    dec = workloads.paged_inputs(seed=77, lengths=[1, 500, 64, 2000], q_lens=[1] * 4, q_heads=32, kv_heads=2,
+                                 head_dim=128, dtype=torch.bfloat16, num_blocks=200, max_blocks=128, device=DEV)
+    dec.block_table[1, 3] = -7
+    dec.block_table[3, 100] = 200
+    dec.block_table[2, 3] = -1                   # the last live block of a 64-key sequence
+    ref = oracle_paged(dec)
+    for s in (0, 1, 8):
+        out = torch.full_like(dec.q, float("nan"))
+        pkv.paged_decode_attn(out, dec.q, dec.k_cache, dec.v_cache, dec.block_table, dec.seqused_k,
+                              max_seqlen_k=dec.max_seqlen_k, softmax_scale=dec.scale, num_splits=s)
+        torch.cuda.synchronize()
+        check_close(out, ref, "bf16", f"G=16 splits={s}")
+
+
+def test_nonfinite_value_in_hidden_live_key():
+    """A NaN V row in a live key that the causal rule hides from most rows of a
+    multi-row unit: the rows that see it come out NaN for that kv head's q heads,
+    every other kv head and every other unit is unaffected and matches the
+    oracle; only the rows the oracle marks unspecified are left out."""
+    inp = workloads.paged_inputs(seed=78, lengths=[90, 200], q_lens=[24, 40], q_heads=16, kv_heads=4,
+                                 head_dim=128, dtype=torch.bfloat16, num_blocks=24, max_blocks=16,
+                                 causal=True, device=DEV)
+    bt = inp.block_table.cpu()
+    j = 85                                        # seen by rows 19..23 of unit 0 only
+    inp.v_cache[int(bt[0, j // 16]), j % 16, 1, 7] = float("nan")
+    inp.k_cache[int(bt[1, 190 // 16]), 190 % 16, 2, 3] = float("nan")   # a NaN score for rows 30.. of unit 1
+    ref, unspec = oracle_paged(inp, with_unspecified=True)
+    assert unspec[:19, 4:8].all() and not unspec[19:24].any() and not unspec[24:].any()
+    assert np.isnan(ref[19:24, 4:8]).any() and np.isnan(ref[24 + 30:, 8:12]).all()
+    for s in (0, 1, 3):
+        check_close(run_varlen_paged(inp, num_splits=s), ref, "bf16", f"splits={s}", skip=unspec)
+
+
+def test_mfma_tickets_back_to_zero():
+    """The matrix-core path's split-K arrival counters (after the vector path's
+    in the workspace) all read 0 after every call, so one workspace serves calls
+    of different split counts."""
+    inp = workloads.paged_inputs(seed=79, lengths=[700, 300, 1500], q_lens=[16, 40, 64], q_heads=32,
+                                 kv_heads=8, head_dim=128, dtype=torch.bfloat16, num_blocks=200,
+                                 max_blocks=100, causal=True, device=DEV)
+    ref = oracle_paged(inp)
+    ws = torch.zeros(pkv.attn_workspace_bytes(3, 64, inp.max_seqlen_k, 32, 8, 128, 64), dtype=torch.uint8,
+                     device=DEV)
+    tiles = (64 * 4 + 127) // 128
+    vec_tickets = 3 * 8 * 256
+    mfma = ws[vec_tickets:vec_tickets + 3 * tiles * 8 * 256].view(torch.int32)[::64]
+    for s in (5, 64, 2, 5):
+        out = torch.full_like(inp.q, float("nan"))
+        pkv.varlen_attn(out, inp.q, inp.k_cache, inp.v_cache, cu_seqlens_q=inp.cu_seqlens_q,
+                        seqused_k=inp.seqused_k, block_table=inp.block_table, max_seqlen_q=64,
+                        max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale, causal=True, num_splits=s,
+                        workspace=ws)
+        torch.cuda.synchronize()
+        check_close(out, ref, "bf16", f"splits={s}")
+        assert int(mfma.abs().sum()) == 0 and int(ws[:vec_tickets].view(torch.int32).abs().sum()) == 0, s
