@@ -322,6 +322,40 @@ pkv_status pkv_column_copy(void* k, void* v, int32_t rows, int32_t cols, int32_t
                            pkv_dtype dtype, void* stream);
 
 /*
+ * pkv_paged_decode_attn_noalloc -- pkv_paged_decode_attn for callers that cannot
+ * allocate device memory: code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, meaning and results as
+ * pkv_paged_decode_attn, without the workspace.
+ *
+ * Its split-K scratch is a static device array of PKV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends; the
+ * call allocates and frees nothing.
+ *  - A call whose arguments need more scratch than that
+ *    (pkv_attn_workspace_bytes with the same arguments) returns PKV_EWORKSPACE
+ *    before enqueuing anything: pass a smaller num_splits, or use
+ *    pkv_paged_decode_attn with a caller workspace.
+ *  - Each call first clears the scratch's split-K arrival counters with a
+ *    small kernel on `stream` (the array keeps the previous call's contents),
+ *    then enqueues the attention as pkv_paged_decode_attn does.
+ *  - Every call on one GPU uses the same array: calls that overlap in time on
+ *    one GPU (other streams, other host threads) race and give undefined
+ *    results.  Order them, e.g. on one stream.
+ *  - The first call on a device looks up the array's address there
+ *    (hipGetSymbolAddress); make that first call outside stream capture.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+pkv_status pkv_paged_decode_attn_noalloc(void* out, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         int32_t num_blocks, int32_t block_size,
+                                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                                         const int32_t* seqused_k, int32_t num_seqs,
+                                         int32_t max_seqlen_k, const void* k_new, const void* v_new,
+                                         int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                         float softmax_scale, int32_t causal, int32_t window,
+                                         const int32_t* kv_start, int32_t num_splits,
+                                         pkv_dtype dtype, void* stream);
+
+/*
  * pkv_attn_workspace_bytes -- device scratch an attention call with these host
  * arguments needs (split-K partials); 0 when it needs none.  `units` is num_seqs
  * (paged) or num_segments (column); num_splits as passed to the call.  With

@@ -18,6 +18,7 @@ __all__ = [
     "PagedKVError", "BLOCK_SIZE", "lib", "library_path", "kv_append", "paged_decode_attn",
     "varlen_attn", "prefix_import", "prefix_export", "column_copy", "BatchControl",
     "attn_workspace_bytes", "attn_num_splits", "status_string", "last_error", "EXPORTED_SYMBOLS",
+    "paged_decode_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 BLOCK_SIZE = 16
@@ -34,7 +35,12 @@ EXPORTED_SYMBOLS = (
     "pkv_batch_rows", "pkv_batch_rows_needed", "pkv_batch_seq_new", "pkv_batch_seq_rm",
     "pkv_batch_seq_clone", "pkv_batch_rewind", "pkv_batch_pos", "pkv_batch_floor",
     "pkv_batch_declare_step", "pkv_batch_prepare_step", "pkv_batch_commit_step", "pkv_column_copy",
+    "pkv_paged_decode_attn_noalloc",
 )
+
+# Bytes of the static split-K scratch behind paged_decode_attn_noalloc (the
+# header's PKV_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PagedKVError(ValueError):
@@ -58,6 +64,9 @@ _SIGS = {
     "pkv_paged_decode_attn": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
                                      _vp, _vp, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _i32, _vp,
                                      _sz, _i32, _vp]),
+    "pkv_paged_decode_attn_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
+                                             _i32, _vp, _vp, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
+                                             _i32, _i32, _vp]),
     "pkv_varlen_attn": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                _i32, _vp, _i32, _vp, _sz, _i32, _vp]),
@@ -351,6 +360,40 @@ def paged_decode_attn(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
         block_table.shape[1], _ptr(seqused_k), B, int(max_seqlen_k), _ptr(k_new), _ptr(v_new),
         Hq, Hkv, D, scale, int(bool(causal)), int(window), _ptr(kv_start), int(num_splits),
         _ptr(workspace), ws_bytes, _dtype(q), _stream(q)))
+    return out
+
+
+def paged_decode_attn_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                              v_cache: torch.Tensor, block_table: torch.Tensor, seqused_k: torch.Tensor,
+                              max_seqlen_k: int, softmax_scale: Optional[float] = None,
+                              causal: bool = False, window: int = 0, num_splits: int = 0,
+                              k_new: Optional[torch.Tensor] = None,
+                              v_new: Optional[torch.Tensor] = None,
+                              kv_start: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``paged_decode_attn`` without a workspace: the library's static device
+    scratch (``NOALLOC_SCRATCH_BYTES`` per GPU) holds the split-K partials, so
+    nothing is allocated.  Calls that overlap in time on one GPU race."""
+    _dev(out, q, k_cache, v_cache, block_table, seqused_k, k_new, v_new, kv_start)
+    _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, Hq, D]")
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "caches must be [NB, 16, Hkv, D]")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [B, W]")
+    _need(seqused_k.dtype == torch.int32, "seqused_k must be int32")
+    B, Hq, D = q.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    _need(Dk == D and block_table.shape[0] == B and seqused_k.numel() == B, "shape mismatch")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype == out.dtype, "dtypes differ")
+    if k_new is not None or v_new is not None:
+        _need(k_new is not None and v_new is not None, "give both k_new and v_new")
+        _need(tuple(k_new.shape) == (B, Hkv, D) and k_new.shape == v_new.shape, "k_new/v_new must be [B, Hkv, D]")
+        _need(k_new.dtype == v_new.dtype == q.dtype, "dtypes differ")
+    if kv_start is not None:
+        _need(kv_start.dtype == torch.int32 and kv_start.numel() == B, "kv_start must be int32 [B]")
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check(lib().pkv_paged_decode_attn_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), NB, BS, _ptr(block_table),
+        block_table.shape[1], _ptr(seqused_k), B, int(max_seqlen_k), _ptr(k_new), _ptr(v_new),
+        Hq, Hkv, D, scale, int(bool(causal)), int(window), _ptr(kv_start), int(num_splits),
+        _dtype(q), _stream(q)))
     return out
 
 

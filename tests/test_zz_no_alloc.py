@@ -1,0 +1,96 @@
+"""pkv_paged_decode_attn_noalloc through the C ABI against pkv_paged_decode_attn.
+
+The no-allocation entry point keeps its split-K scratch in a static device
+array shared by every call on the GPU.  Each call here goes through ctypes to
+the raw symbol and must give the same bits as the workspace entry point on the
+same inputs (same kernels, same split count), and match the oracle.  Calls of
+different sizes follow one another, so a call's arrival counters sit where an
+earlier call left partials.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+import torch
+
+import paged_kv_cache_194_amd as pkv
+import workloads
+from helpers import bits, check_close, oracle_paged, paged_slots
+
+BF16 = 1
+
+
+def _noalloc(out, inp, num_splits=0, k_new=None, v_new=None):
+    B, Hq, D = inp.q.shape
+    NB, BS, Hkv, _ = inp.k_cache.shape
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())   # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return pkv.lib().pkv_paged_decode_attn_noalloc(
+        p(out), p(inp.q), p(inp.k_cache), p(inp.v_cache), NB, BS, p(inp.block_table),
+        inp.block_table.shape[1], p(inp.seqused_k), B, int(inp.max_seqlen_k), p(k_new), p(v_new),
+        Hq, Hkv, D, float(inp.scale), 0, 0, None, int(num_splits), BF16, stream)
+
+
+def _with_workspace(inp, num_splits=0, k_new=None, v_new=None):
+    out = torch.full_like(inp.q, float("nan"))
+    pkv.paged_decode_attn(out, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seqused_k,
+                          max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale,
+                          num_splits=num_splits, k_new=k_new, v_new=v_new)
+    return out
+
+
+def _case(seed, lengths):
+    return workloads.paged_inputs(seed=seed, lengths=lengths, q_lens=[1] * len(lengths), q_heads=32,
+                                  kv_heads=8, head_dim=128, dtype=torch.bfloat16,
+                                  num_blocks=sum((E + 15) // 16 for E in lengths) + 8,
+                                  max_blocks=max((E + 15) // 16 for E in lengths) + 2, device="cuda:0")
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_workspace_entry_point():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    big = _case(701, [int(x) for x in torch.randint(1, 3000, (48,), generator=torch.Generator().manual_seed(7))])
+    small = _case(702, [900, 17, 1, 2500])
+    # big, then smaller (its partials land inside the big call's counter area), then big again
+    for name, inp, splits in (("big", big, 0), ("small", small, 0), ("big again", big, 0),
+                              ("small, 16 splits", small, 16)):
+        out = torch.full_like(inp.q, float("nan"))
+        st = _noalloc(out, inp, splits)
+        assert st == 0, (name, pkv.last_error())
+        torch.cuda.synchronize()
+        ref_out = _with_workspace(inp, splits)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), bits(ref_out)), name
+        check_close(out, oracle_paged(inp), "bf16", name)
+
+
+@pytest.mark.gpu
+def test_noalloc_fused_append_matches():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    a = _case(703, [4096])
+    b = _case(703, [4096])
+    kn = torch.randn(a.k_new.shape, generator=torch.Generator().manual_seed(5)).to("cuda:0", torch.bfloat16)
+    vn = torch.randn(a.k_new.shape, generator=torch.Generator().manual_seed(6)).to("cuda:0", torch.bfloat16)
+    out = torch.full_like(a.q, float("nan"))
+    assert _noalloc(out, a, 0, kn, vn) == 0, pkv.last_error()
+    ref_out = _with_workspace(b, 0, kn, vn)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(ref_out))
+    assert torch.equal(bits(a.k_cache), bits(b.k_cache)) and torch.equal(bits(a.v_cache), bits(b.v_cache))
+    slot = int(paged_slots(a)[0])
+    assert torch.equal(bits(a.k_cache.view(-1, 8, 128)[slot]), bits(kn[0]))
+
+
+def test_noalloc_rejects_oversized_plan_before_enqueueing():
+    """A plan larger than the static scratch is refused on the host (no device
+    memory is touched: the pointers are never dereferenced)."""
+    fake = ctypes.c_void_p(16)
+    need = pkv.attn_workspace_bytes(64, 1, 8192, 32, 8, 128, 256)
+    assert need > pkv.NOALLOC_SCRATCH_BYTES
+    st = pkv.lib().pkv_paged_decode_attn_noalloc(
+        fake, fake, fake, fake, 40000, 16, fake, 512, fake, 64, 8192, None, None, 32, 8, 128,
+        0.088, 0, 0, None, 256, BF16, None)
+    assert st == 3 and "static scratch" in pkv.last_error()
