@@ -81,6 +81,21 @@ def cpu_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def host_info() -> dict:
+    """Cores the oracle may use and what they are."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cpus": len(os.sched_getaffinity(0)), "blas_threads": cpu_threads(),
+            "cpu_model": model}
+
+
 def copy_ceiling_gbs(torch, nbytes=4 << 30, reps=5) -> float:
     """A plain device-to-device copy: read + write bytes over time."""
     a = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
@@ -108,6 +123,25 @@ def time_graph(torch, graph, reps: int) -> float:
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / 1e3 / reps
+
+
+def time_call(torch, fn, args) -> float:
+    """Average seconds per call: graph replays, or with --eager plain launches
+    (hardware counters are taken per dispatch)."""
+    if args.eager:
+        for _ in range(max(1, args.warmup)):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(args.steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / 1e3 / args.steps
+    g = capture(torch, fn)
+    time_graph(torch, g, max(1, args.warmup))
+    return time_graph(torch, g, args.steps)
 
 
 def capture(torch, fn):
@@ -175,8 +209,6 @@ def bench_decode_step(args, torch):
     ws = cache.workspace
     if args.eager:
         result_eager = {"metric": METRIC, "eager_us_per_step": round(sec_step * 1e6, 2), "wall_s": round(wall, 3)}
-        if args.copy_ceiling:
-            result_eager["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
         return result_eager
 
     def attn_only():
@@ -218,8 +250,6 @@ def bench_decode_step(args, torch):
                      "bytes_per_launch": kv_bytes_layer, "us_per_launch": round(sec_call * 1e6, 3)},
         "wall_s_timed": round(wall, 4),
     }
-    if args.copy_ceiling:
-        result["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(args, torch, cache, inputs, L, kv_bytes_step)
     return result
@@ -248,7 +278,7 @@ def cpu_baseline_decode(args, torch, cache, inputs, L, kv_bytes_step):
                                max_seqlen_k=cache.bucket)
     sec = (time.perf_counter() - t0) / len(layers) * m_layers
     return {"value": round(kv_bytes_step / sec / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
-            "kind": "oracle", "sec_per_step": round(sec, 3),
+            "kind": "oracle", "sec_per_step": round(sec, 3), **host_info(),
             "sample": f"{len(layers)} of {m_layers} layers of one step at {L} keys, scaled to the step"}
 
 
@@ -298,9 +328,7 @@ def bench_single_call(args, torch):
         return bench_multirow(args, torch)
     else:
         raise SystemExit(f"unknown --config {args.config}")
-    g = capture(torch, call)
-    time_graph(torch, g, max(1, args.warmup))
-    sec = time_graph(torch, g, args.steps)
+    sec = time_call(torch, call, args)
     gbs = kv_bytes / sec / 1e9
     return {"metric": f"{name}: KV GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
@@ -362,8 +390,6 @@ def bench_prefix(args, torch):
         torch.cuda.synchronize()
         res = {"metric": "prefill hand-over copy GB/s (import + export)",
                "eager_us_per_step": round(s.elapsed_time(e) * 1e3 / args.steps, 2)}
-        if args.copy_ceiling:
-            res["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
         return res
     g = capture(torch, step)
     time_graph(torch, g, max(1, args.warmup))
@@ -401,8 +427,6 @@ def bench_prefix(args, torch):
                                "frac": round(per_launch / sec_exp / 1e9 / HBM_PEAK_GBS, 4),
                                "us_per_launch": round(sec_exp * 1e6, 3)},
            "wall_s_timed": round(wall, 4)}
-    if args.copy_ceiling:
-        res["copy_ceiling_gbs"] = round(copy_ceiling_gbs(torch), 1)
     if not args.no_cpu_baseline:
         import oracle
         layers = list(range(min(m.layers, args.cpu_layers)))
@@ -418,6 +442,7 @@ def bench_prefix(args, torch):
         csec = (time.perf_counter() - t0) / len(layers) * m.layers
         res["cpu_baseline"] = {"value": round(step_bytes / csec / 1e9, 4), "unit": "GB/s",
                                "cores": cpu_threads(), "kind": "oracle", "sec_per_step": round(csec, 3),
+                               **host_info(),
                                "sample": f"import + export of {len(layers)} of {m.layers} layers, "
                                          "scaled to the step"}
     return res
@@ -485,9 +510,7 @@ def bench_multirow(args, torch):
         pairs += p_u
     kv_bytes = keys * inp.kv_heads * inp.head_dim * 2 * 2
     flops = 4 * inp.head_dim * inp.q_heads * pairs
-    g = capture(torch, call)
-    time_graph(torch, g, max(1, args.warmup))
-    sec = time_graph(torch, g, args.steps)
+    sec = time_call(torch, call, args)
     gbs, tfs = kv_bytes / sec / 1e9, flops / sec / 1e12
     hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tfs / 2500.0
     bound = "hbm" if kv_bytes / (HBM_PEAK_GBS * 1e9) >= flops / 2.5e15 else "mfma"
@@ -514,9 +537,11 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split-K partitions (0: library choice)")
     ap.add_argument("--cpu-layers", type=int, default=42, help="layers the CPU oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-ceiling", action="store_true", help="also time a 4 GiB device copy")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip the 4 GiB device copy timed as the practical HBM ceiling")
+    ap.add_argument("--copy-ceiling", action="store_true", help="time the device copy (the default)")
     ap.add_argument("--eager", action="store_true",
-                    help="c2 and prefix: plain launches instead of graph replays (for per-dispatch counters)")
+                    help="plain launches instead of graph replays (for per-dispatch counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
@@ -533,6 +558,11 @@ def main():
         res = bench_prefix(args, torch)
     else:
         res = bench_single_call(args, torch)
+    if not args.no_copy_ceiling:
+        ceil = copy_ceiling_gbs(torch)
+        res["copy_ceiling_gbs"] = round(ceil, 1)
+        if "value" in res and res.get("unit") == "GB/s":
+            res["pct_copy_ceiling"] = round(100 * res["value"] / ceil, 2)
     print(json.dumps(res), flush=True)
 
 
