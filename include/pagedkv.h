@@ -143,10 +143,16 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  *                units.
  * workspace    : device scratch of at least pkv_attn_workspace_bytes(num_seqs, 1,
  *                max_seqlen_k, q_heads, kv_heads, head_dim, num_splits) bytes
- *                (may be NULL when that is 0).  Zero-fill it once before its
- *                first use: it starts with split-K arrival counters that every
- *                call leaves at zero again.  Calls that share a workspace must
- *                not run concurrently (one stream, or ordered streams).
+ *                (may be NULL when that is 0).  It starts with split-K arrival
+ *                counters, one 256-byte line per (sequence, kv head), that every
+ *                call leaves at zero; the partials follow them.  Zero-fill it
+ *                before its first use, and again before a call with another
+ *                number of sequences or kv heads (or, for pkv_varlen_attn,
+ *                another max_seqlen_q or head_dim) reuses it, since the counters
+ *                then sit elsewhere; calls that differ only in lengths,
+ *                num_splits or max_seqlen_k need no refill.  Calls that share a
+ *                workspace must not run concurrently (one stream, or ordered
+ *                streams).
  */
 pkv_status pkv_paged_decode_attn(void* out, const void* q,
                                  const void* k_cache, const void* v_cache,

@@ -524,3 +524,28 @@ def test_split_tickets_reset_and_workspace_reuse():
                 first = out.clone()
             else:
                 assert torch.equal(bits(out), bits(first))
+
+
+def test_single_sequence_split_counts_share_one_workspace():
+    """One sequence, one zero-filled workspace, a run of calls with different
+    split counts (empty splits included): every kv head's arrival counter is
+    back at zero after each call, and equal split counts give equal bits."""
+    H = 8
+    inp = workloads.paged_inputs(seed=82, lengths=[1000], q_lens=[1], q_heads=32, kv_heads=H, head_dim=128,
+                                 dtype=torch.bfloat16, num_blocks=70, max_blocks=64, device=DEV)
+    ref = oracle_paged(inp)
+    ws = torch.zeros(pkv.attn_workspace_bytes(1, 1, inp.max_seqlen_k, 32, H, 128, 256), dtype=torch.uint8,
+                     device=DEV)
+    tickets = ws[:H * 256].view(torch.int32)[::64]
+    seen = {}
+    for s in (64, 2, 7, 256, 64, 1, 33, 2, 256):
+        out = run_decode(inp, num_splits=s, workspace=ws)
+        check_close(out, ref, "bf16", f"splits={s}")
+        assert int(tickets.abs().sum()) == 0, f"splits={s}: {tickets.tolist()}"
+        if s in seen:
+            assert torch.equal(bits(out), bits(seen[s])), f"splits={s} repeat"
+        seen[s] = out.clone()
+    short = workloads.paged_inputs(seed=83, lengths=[5], q_lens=[1], q_heads=32, kv_heads=H, head_dim=128,
+                                   dtype=torch.bfloat16, num_blocks=8, max_blocks=64, device=DEV)
+    for s in (32, 256):
+        check_close(run_decode(short, num_splits=s, workspace=ws), oracle_paged(short), "bf16", f"E=5 splits={s}")

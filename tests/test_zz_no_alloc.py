@@ -53,9 +53,12 @@ def test_noalloc_matches_workspace_entry_point():
         pytest.skip("needs a GPU")
     big = _case(701, [int(x) for x in torch.randint(1, 3000, (48,), generator=torch.Generator().manual_seed(7))])
     small = _case(702, [900, 17, 1, 2500])
-    # big, then smaller (its partials land inside the big call's counter area), then big again
+    one = _case(704, [3000])
+    # big, then smaller, then big again; single sequences (the workspace entry point
+    # takes the tagged hand-off there, this one the acknowledged: same bits)
     for name, inp, splits in (("big", big, 0), ("small", small, 0), ("big again", big, 0),
-                              ("small, 16 splits", small, 16)):
+                              ("small, 16 splits", small, 16), ("one sequence", one, 0),
+                              ("one sequence, 7 splits", one, 7), ("big, last", big, 0)):
         out = torch.full_like(inp.q, float("nan"))
         st = _noalloc(out, inp, splits)
         assert st == 0, (name, pkv.last_error())
