@@ -120,8 +120,12 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  * max_seqlen_k : host bound on seqused_k (the bucket).
  * k_new, v_new : optional [num_seqs, kv_heads, head_dim].  When both are given,
  *                the call first appends them at position seqused_k[b] - 1 of
- *                each sequence (the slot found through block_table) and then
- *                attends, as one step.  When NULL the cache is only read.
+ *                each sequence (the slot found through block_table; nothing for
+ *                an empty sequence or an entry outside the pool) and then
+ *                attends, as one step: inside the attention kernel for
+ *                q_heads / kv_heads <= 8, as a launch of its own before the
+ *                matrix-core attention above that.  When NULL the cache is only
+ *                read.
  * softmax_scale: multiplies q.k before the softmax.
  * causal       : with one query per sequence causal equals non-causal.
  * window       : > 0 keeps the last `window` keys (p - window + 1 .. p).
@@ -192,6 +196,10 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q,
  * Other arguments as for pkv_paged_decode_attn.  workspace must hold
  * pkv_attn_workspace_bytes(units, max_seqlen_q, ...) bytes with units =
  * num_seqs or num_segments.
+ * Kernels: bf16 units of one query row (and GQA groups <= 8) run on the vector
+ * path, bf16 units of several rows (or groups > 8) on the matrix cores; fp32
+ * takes every covered query row as a single query on the vector path (fp32
+ * products throughout), groups <= 8 only (PKV_EUNSUPPORTED above).
  */
 pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q,
                            const void* k, const void* v,

@@ -157,6 +157,14 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
 // Bytes at the start of the workspace that hold arrival counters.
 size_t plan_ticket_bytes(const Plan& pl) { return pl.vec_ticket + pl.mfma_ticket; }
 
+// Row mode (fp32 calls with several query rows per unit): the vector path
+// takes every row of every unit as its own single-query item, units *
+// max_seqlen_q items in all.
+int64_t row_items(int32_t units, int32_t max_seqlen_q) {
+    return (int64_t)(units > 0 ? units : 1) * (max_seqlen_q > 0 ? max_seqlen_q : 1);
+}
+constexpr int64_t kMaxGridY = 65535;
+
 // Enqueue the attention kernels for a fully checked parameter block.
 pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, const Plan& pl,
                          void* workspace, hipStream_t stream) {
@@ -164,7 +172,15 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
     p.num_splits = pl.splits;
     p.ws_ticket = nullptr;
     p.ws_o = p.ws_ml = nullptr;
-    p.vec_wgs = pkv::vec_slots(p.num_units, pl.splits);
+    p.vec_units = p.row_mode ? (int32_t)row_items(p.num_units, p.max_seqlen_q) : p.num_units;
+    p.vec_wgs = pkv::vec_slots(p.vec_units, pl.splits);
+    if (pl.vec && p.num_units > 0 && p.vec_wgs > kMaxGridY)
+        return fail(PKV_EUNSUPPORTED, "%d vector-path work groups per kv head exceed the grid limit: pass a "
+                    "smaller num_splits", p.vec_wgs);
+    if (pl.mfma && p.num_units > 0 &&
+        (int64_t)pl.tiles * pl.msplits * (pl.msplits > 1 && (int64_t)p.num_units * pl.tiles > 1 ? p.num_units : 1) >
+            kMaxGridY)
+        return fail(PKV_EUNSUPPORTED, "too many matrix-core work groups per kv head: pass a smaller num_splits");
     char* partials = ws + plan_ticket_bytes(pl);
     if (pl.vec_bytes) {
         const size_t n = (size_t)p.vec_wgs * p.kv_heads * pl.gt;
@@ -303,7 +319,14 @@ size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max
                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                 int32_t num_splits) {
     if (units <= 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || head_dim <= 0) return 0;
-    return make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).ws_bytes;
+    size_t need = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).ws_bytes;
+    // An fp32 call with several rows per unit runs in row mode: cover that plan too.
+    const int64_t items = row_items(units, max_seqlen_q);
+    if (max_seqlen_q > 1 && q_heads / kv_heads <= kVecMaxGroup && items <= INT32_MAX) {
+        const size_t rows = make_plan((int32_t)items, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).ws_bytes;
+        if (rows > need) need = rows;
+    }
+    return need;
 }
 
 int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -337,8 +360,6 @@ pkv_status decode_check(void* out, const void* q, const void* k_cache, const voi
     const int32_t group = q_heads / kv_heads;
     if (group > kVecMaxGroup && !pkv::attn_mfma_supported(dtype, head_dim))
         return fail(PKV_EUNSUPPORTED, "q_heads / kv_heads = %d > 8 needs bf16 (matrix-core path)", group);
-    if (group > kVecMaxGroup && k_new)
-        return fail(PKV_EUNSUPPORTED, "fused append with q_heads / kv_heads > 8: call pkv_kv_append first");
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !seqused_k)
         return fail(PKV_EINVAL, "null pointer argument");
@@ -377,8 +398,19 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, 
     const int32_t kv_cap = (int32_t)(cap64 < max_seqlen_k ? cap64 : max_seqlen_k);
     hipStream_t st = (hipStream_t)stream;
     pkv::AttnParams p{};
-    p.k_new = k_new;       // appended inside the attention kernel
-    p.v_new = v_new;
+    // The vector kernel appends inside the attention; a group above 8 runs on
+    // the matrix cores, so the append goes first as its own launch.
+    const bool append_first = k_new && !pl.vec;
+    if (append_first) {
+        pkv_status s2 = hip_status(
+            pkv::launch_decode_append(const_cast<void*>(k_cache), const_cast<void*>(v_cache), num_blocks, k_new,
+                                      v_new, num_seqs, (int64_t)kv_heads * head_dim * elem_bytes(dtype),
+                                      seqused_k, kv_cap, block_table, max_blocks_per_seq, st),
+            "decode append");
+        if (s2 != PKV_OK) return s2;
+    }
+    p.k_new = append_first ? nullptr : k_new;
+    p.v_new = append_first ? nullptr : v_new;
     p.out = out;
     p.q = q;
     p.k = k_cache;
@@ -441,12 +473,17 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q, const void
         units = num_segments;
     }
     const int32_t group = q_heads / kv_heads;
-    if ((max_seqlen_q > 1 || group > kVecMaxGroup) && !pkv::attn_mfma_supported(dtype, head_dim))
-        return fail(PKV_EUNSUPPORTED, "multi-row units (max_seqlen_q %d, group %d) run on the bf16 matrix-core path",
-                    max_seqlen_q, group);
+    if (group > kVecMaxGroup && !pkv::attn_mfma_supported(dtype, head_dim))
+        return fail(PKV_EUNSUPPORTED, "q_heads / kv_heads = %d > 8 runs on the bf16 matrix-core path only", group);
+    // fp32 with several rows per unit: every row on the vector path (row mode).
+    const bool row_mode = max_seqlen_q > 1 && !pkv::attn_mfma_supported(dtype, head_dim);
+    if (row_mode && row_items(units, max_seqlen_q) > INT32_MAX)
+        return fail(PKV_EUNSUPPORTED, "units * max_seqlen_q too large for the fp32 row path");
     if (total_q == 0) return ok();
     if (!out || !q || !k || !v) return fail(PKV_EINVAL, "null pointer argument");
-    const Plan pl = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    const Plan pl = row_mode ? make_plan((int32_t)row_items(units, max_seqlen_q), 1, max_seqlen_k, q_heads, kv_heads,
+                                         head_dim, num_splits)
+                             : make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
     if (workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !workspace))
         return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.ws_bytes);
 
@@ -465,6 +502,7 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q, const void
     p.window = w;
     p.kv_start = kv_start;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.row_mode = row_mode ? 1 : 0;
     if (paged) {
         p.mode = pkv::kPagedVarlen;
         p.cu_seqlens_q = cu_seqlens_q;

@@ -82,17 +82,49 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     }
 }
 
-// Whether the vector path computes unit ui: a unit of one query row, or the
-// first row of any unit when the call's static bound max_seqlen_q is 1 (the
-// matrix-core path takes the other multi-row units).
+// The vector path's work item w.  Normally a unit.  In row mode (fp32 calls
+// with several query rows per unit) item w is row i = w % max_seqlen_q of unit
+// w / max_seqlen_q, seen as a single query: q_start moves to that row and
+// q_len becomes L - i, so that its position E - q_len is the row's E - L + i;
+// a row past the unit's rows (or past max_seqlen_q) gets q_len 0.  `tab` is
+// the unit whose block-table row or column the keys come from.
+struct VecItem {
+    UnitInfo ui;
+    int32_t tab;
+};
+__device__ __forceinline__ VecItem load_vec_item(const AttnParams& p, int32_t w) {
+    VecItem it;
+    if (!p.row_mode) {
+        it.tab = w;
+        it.ui = load_unit(p, w);
+        return it;
+    }
+    const int32_t R = p.max_seqlen_q;
+    it.tab = w / R;
+    const int32_t i = w - it.tab * R;
+    it.ui = load_unit(p, it.tab);
+    const int32_t L = it.ui.q_len < R ? it.ui.q_len : R;
+    if (i >= L) {
+        it.ui.q_len = 0;
+    } else {
+        it.ui.q_start += i;
+        it.ui.q_len -= i;
+    }
+    return it;
+}
+
+// Whether the vector path computes an item: a unit of one query row, the first
+// row of any unit when the call's static bound max_seqlen_q is 1 (the
+// matrix-core path takes the other multi-row units), or any covered row in
+// row mode.
 __device__ __forceinline__ bool vec_takes(const AttnParams& p, const UnitInfo& ui) {
-    return ui.q_len == 1 || (ui.q_len > 1 && p.max_seqlen_q == 1);
+    return ui.q_len == 1 || (ui.q_len > 1 && (p.max_seqlen_q == 1 || p.row_mode));
 }
 
 // Live 16-key blocks of unit u for the vector path, or -1 when the unit is
 // not this path's (see vec_takes, or its row outside the output).
 __device__ __forceinline__ int32_t vec_unit_blocks(const AttnParams& p, int32_t u) {
-    const UnitInfo ui = load_unit(p, u);
+    const UnitInfo ui = load_vec_item(p, u).ui;
     if (!vec_takes(p, ui) || ui.q_start < 0 || ui.q_start >= p.total_q) return -1;
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
     const KeyRange kr = first_row_keys(p, E, ui.q_len, ui.pad);
@@ -221,13 +253,13 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     //    least one, so an empty unit still writes its zero row), c the smallest
     //    block count per slot for which the deal fits the slots.
     int32_t u, split, S, slot0;
-    if (p.num_units == 1) {
+    if (p.vec_units == 1) {
         u = 0; split = slot; S = p.num_splits; slot0 = 0;
     } else if (p.num_splits == 1) {
         u = slot; split = 0; S = 1; slot0 = u;
     } else {
         if (wave == 0) {
-            const int32_t U = p.num_units;
+            const int32_t U = p.vec_units;
             const int64_t W = (int64_t)p.num_splits * U;
             const int32_t per = (U + 63) / 64;
             const int32_t ub = lane * per, ue = min(U, ub + per);
@@ -258,7 +290,9 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
         if (u < 0) return;                          // a spare slot
     }
 
-    const UnitInfo ui = load_unit(p, u);
+    const VecItem item = load_vec_item(p, u);
+    const UnitInfo& ui = item.ui;
+    const int64_t tab_row = (int64_t)item.tab * p.max_blocks;   // block-table row (paged)
     if (!vec_takes(p, ui)) return;                  // other units are not this path's
     const int32_t row = ui.q_start;
     if (row < 0 || row >= p.total_q) return;
@@ -280,7 +314,7 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     int32_t ids = -1;               // lane i: pool block of this wave's i-th block
     if constexpr (PAGED) {
         const int32_t blk = sb + wave + kWaves * lane;
-        if (blk < se) ids = p.block_table[(int64_t)u * p.max_blocks + blk];
+        if (blk < se) ids = p.block_table[tab_row + blk];
     }
     // Blocks of this wave: first + 4 i, i < nb.
     const int32_t first = sb + wave;
@@ -347,7 +381,7 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     // wave per SIMD (whose loop would otherwise carry the store's operands).
     const int32_t pblk = pn >> 4, ptt = pn & 15;
     const bool own_new = fuse && pblk >= sb && pblk < se && (pblk - sb) % kWaves == wave;
-    const int32_t pid = (own_new && PAGED) ? p.block_table[(int64_t)u * p.max_blocks + pblk] : 0;
+    const int32_t pid = (own_new && PAGED) ? p.block_table[tab_row + pblk] : 0;
     constexpr bool kStoreAfter = vec_waves_per_simd<T, D, GT>() == 2;
     auto store_new_row = [&]() {
         if (own_new && id_ok(pid) && lane < D * EB / 16) {
@@ -513,7 +547,7 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
             if constexpr (PAGED) {
                 if (g0 > 0) {
                     const int32_t blk = first + kWaves * (g0 + lane);
-                    ids = lane < gn ? p.block_table[(int64_t)u * p.max_blocks + blk] : -1;
+                    ids = lane < gn ? p.block_table[tab_row + blk] : -1;
                 }
             }
             auto id_of = [&](int k) -> int32_t { return PAGED ? __builtin_amdgcn_readlane(ids, k) : 0; };

@@ -52,6 +52,8 @@ struct AttnParams {
     int32_t window;
     int32_t num_splits;    // vector path: split-K partitions per unit (on average)
     int32_t vec_wgs;       // vector path: work-group slots per kv head
+    int32_t vec_units;     // vector path: work items (units, or unit rows in row mode)
+    int32_t row_mode;      // vector path takes each row of a unit as its own item
     float scale_log2;      // softmax_scale * log2(e)
 };
 
@@ -135,6 +137,14 @@ void clear_error();
 hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
                             const void* k_new, const void* v_new, int32_t num_tokens,
                             const int64_t* slot_mapping, int64_t row_bytes, hipStream_t stream);
+
+// Single-query decode append with the slot found on the device: row b of
+// k_new/v_new to position clamp(seqused_k[b], 0, kv_cap) - 1 through the block
+// table; nothing for an empty sequence or an entry outside the pool.
+hipError_t launch_decode_append(void* k_cache, void* v_cache, int32_t num_blocks, const void* k_new,
+                                const void* v_new, int32_t num_seqs, int64_t row_bytes,
+                                const int32_t* seqused_k, int32_t kv_cap, const int32_t* block_table,
+                                int32_t max_blocks, hipStream_t stream);
 
 // Prefix copies between a dense [batch, heads, src_len, D] cache and paged
 // slots; to_dense = export (then src_len == n and seqused_k is unused).

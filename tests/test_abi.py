@@ -78,7 +78,6 @@ def _decode(**over):
     (dict(nb=0), EINVAL),
     (dict(splits=-2), EINVAL),
     (dict(hq=32, hkv=2, dtype=F32), EUNSUP), # group 16 runs on the bf16 matrix-core path only
-    (dict(hq=32, hkv=2, kn=ctypes.c_void_p(16), vn=ctypes.c_void_p(16)), EUNSUP),  # no fused append there
     (dict(hq=32, hkv=2), EINVAL),            # supported shape: null pointers are next
     (dict(kn=ctypes.c_void_p(16)), EINVAL),  # k_new without v_new
     (dict(scale=float("nan")), EINVAL),
@@ -127,7 +126,13 @@ def test_varlen_host_errors():
     assert _varlen(bt=p, cu=p, used=p, mq=0) == EINVAL
     assert _varlen(bt=p, cu=p, used=p, bs=8) == EINVAL
     assert _varlen(bt=p, cu=None, used=p) == EINVAL
-    assert _varlen(bt=p, cu=p, used=p, mq=4, dtype=F32) == EUNSUP   # multi-row fp32: no kernel
+    assert _varlen(bt=p, cu=p, used=p, mq=4, dtype=F32, hq=32, hkv=2) == EUNSUP   # fp32, group 16: no kernel
+    assert _varlen(bt=p, cu=p, used=p, mq=4, dtype=F32) == EINVAL   # fp32 rows are supported: null out/q/k/v
+    import torch
+    if not torch.cuda.is_available():    # fake pointers only where no GPU could run a launch
+        # an explicit split count whose grid exceeds the launch limit is refused on the host
+        assert _varlen(bt=p, cu=p, used=p, ns=400, mq=1, splits=256, out=p, q=p, k=p, v=p, ws=p,
+                       wsb=1 << 40) == EUNSUP
 
 
 def test_kv_append_host_errors():
