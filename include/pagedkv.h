@@ -380,7 +380,9 @@ size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max
                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                 int32_t num_splits);
 
-/* Split count the library uses for these host arguments (num_splits = 0 picks). */
+/* Split count the library uses for these host arguments (num_splits = 0 picks):
+ * the vector path's for calls of single-row units with groups <= 8, else the
+ * matrix-core path's. */
 int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
                             int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                             int32_t num_splits);

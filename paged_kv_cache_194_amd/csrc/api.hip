@@ -114,15 +114,13 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
     Plan pl{};
     const int32_t group = q_heads / kv_heads;
     const int32_t U = units > 0 ? units : 1;
-    pl.vec = group <= kVecMaxGroup;
+    // A call whose units may have several query rows runs every unit on the
+    // matrix cores, single-row ones included, in one launch: which units have
+    // one row only the device knows, and a separate vector launch would run
+    // after, not beside, the matrix-core one.
+    pl.vec = group <= kVecMaxGroup && max_seqlen_q <= 1;
     pl.mfma = max_seqlen_q > 1 || group > kVecMaxGroup;
     pl.splits = pick_splits(units, kv_heads, keys, num_splits);
-    // With multi-row units in the call the vector path serves only part of
-    // the units (the single-row ones, or none: which, only the device knows),
-    // so its library split count is capped at 4 (column-store step 396 us
-    // against 410 us at the uncapped 8; draft verify, no single-row unit,
-    // 442 us against 446 us).
-    if (num_splits == 0 && max_seqlen_q > 1 && pl.splits > 4) pl.splits = 4;
     pl.gt = pkv::vec_group_rows(group);
     if (pl.vec && pl.splits > 1) {
         pl.vec_ticket = pkv::ticket_bytes(U, kv_heads);
@@ -190,6 +188,7 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
     }
     p.mfma_tiles = pl.tiles;
     p.mfma_splits = pl.msplits;
+    p.mfma_single = pl.mfma && !pl.vec;
     p.mws_ticket = nullptr;
     p.mws_o = p.mws_ml = nullptr;
     if (pl.mfma_bytes) {
@@ -199,12 +198,18 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
         p.mws_ml = p.mws_o + n * head_dim;
     }
     if (p.num_units == 0 && p.total_q == 0) return ok();
-    if (p.mode != pkv::kPagedDecode) {
+    // Rows no unit covers are zeroed inside the attention launch (the
+    // matrix-core one when there is one), or by a launch of their own when
+    // there is no unit to attend.
+    p.zero_rows = (p.mode != pkv::kPagedDecode && p.num_units > 0) ? 1 : 0;
+    if (p.mode != pkv::kPagedDecode && p.num_units == 0) {
         pkv_status s = hip_status(pkv::launch_zero_uncovered(p, dtype, head_dim, stream), "zero rows");
         if (s != PKV_OK) return s;
     }
     if (p.num_units > 0 && pl.vec) {
-        pkv_status s = hip_status(pkv::launch_attn_vec(p, dtype, head_dim, stream), "attention");
+        pkv::AttnParams pv = p;
+        pv.zero_rows = pl.mfma ? 0 : p.zero_rows;
+        pkv_status s = hip_status(pkv::launch_attn_vec(pv, dtype, head_dim, stream), "attention");
         if (s != PKV_OK) return s;
     }
     if (p.num_units > 0 && pl.mfma) {
@@ -333,7 +338,8 @@ int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seq
                             int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                             int32_t num_splits) {
     if (kv_heads <= 0) return 1;
-    return make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).splits;
+    const Plan pl = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    return pl.vec ? pl.splits : pl.msplits;
 }
 
 }  // extern "C"

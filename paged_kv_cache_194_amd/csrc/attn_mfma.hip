@@ -172,7 +172,7 @@ __device__ __forceinline__ int32_t mfma_item_chunks(const AttnParams& p, int32_t
                                                     int32_t bm, int32_t bn) {
     const UnitInfo ui = load_unit(p, u);
     const int32_t L = ui.q_len;
-    if (L <= 0 || (L == 1 && p.group <= 8)) return -1;
+    if (L <= 0 || (L == 1 && p.group <= 8 && !p.mfma_single)) return -1;
     const int32_t M = (L < p.max_seqlen_q ? L : p.max_seqlen_q) * p.group;
     if (tile * bm >= M) return -1;
     return tile_keys(p, ui.keys_ok ? ui.kv_end : 0, L, M, tile * bm, bm, bn, ui.pad).nchunk;
@@ -192,8 +192,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 
     __shared__ int32_t sWork[5];
     const int32_t T = p.mfma_tiles;               // row tiles per (unit, kv head)
-    // kv head fastest: the work groups reading the heads of the same keys run together.
+    // kv head fastest: the work groups reading the heads of the same keys run
+    // together.  Those of kv head 0 also zero their share of uncovered rows.
     const int32_t g = blockIdx.x;
+    if (p.zero_rows && g == 0) zero_rows_share(p, p.q_heads * D * 2, reinterpret_cast<uint32_t*>(&sLast), NT);
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
@@ -247,8 +249,9 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     const UnitInfo ui = load_unit(p, u);
     const int32_t G = p.group;
     const int32_t L = ui.q_len;
-    // Units with one row and a small group belong to the vector path.
-    if (L <= 0 || (L == 1 && G <= 8)) return;
+    // Units with one row and a small group belong to the vector path, unless
+    // this call runs everything here (mfma_single).
+    if (L <= 0 || (L == 1 && G <= 8 && !p.mfma_single)) return;
     const int32_t Lr = L < p.max_seqlen_q ? L : p.max_seqlen_q;   // rows past the bound: uncovered
     const int32_t M = Lr * G;
     const int32_t m0 = tile * BM;
@@ -298,6 +301,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     // Q complete before the pipeline starts: otherwise the first use of qf in the
     // chunk loop would wait for every load in flight.
     wait_vm_all();
+    // A wave none of whose rows exist (a unit of few rows, e.g. one query row
+    // of a small group) still issues its share of every chunk's loads and
+    // meets every barrier, but skips the products.
+    bool any_row = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) any_row |= rows_ok[rt];
+    const bool wave_idle = __ballot(any_row) == 0;
 
     f32x4_t o[RT][DT];
     float m_run[RT], l_run[RT];
@@ -403,6 +413,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     };
 
     auto compute = [&](int32_t c, int st_idx, const uint8_t* sKb, const uint8_t* sVb) __attribute__((always_inline)) {
+        if (wave_idle) return;
         const int32_t c0 = c_base + c * BN;
         const uint32_t bad = (nostore >> (KT * st_idx)) & ((1u << KT) - 1u);   // tiles without storage
         // A wave issues its two MFMA passes at raised priority and its softmax at

@@ -237,8 +237,13 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     __shared__ int32_t sWork[4];
 
     // The kv head is the fastest grid dimension: the work groups reading the
-    // heads of the same blocks run together and share DRAM rows.
+    // heads of the same blocks run together and share DRAM rows.  Those of kv
+    // head 0 also zero their share of the rows no unit covers.
     const int32_t g = blockIdx.x;
+    if (p.zero_rows && g == 0) {
+        __shared__ uint32_t sTodo;
+        zero_rows_share(p, p.q_heads * D * (int32_t)sizeof(T), &sTodo, kThreads);
+    }
     const int32_t slot = blockIdx.y;
     const int lane = lane_id();
     const int wave = threadIdx.x >> 6;
@@ -670,55 +675,15 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
     merge_splits<T, D, GT>(p, g, row, slot0, S);
 }
 
-// Zero the output rows that no unit covers.  A work group takes kZeroRows
-// rows: wave 0 reads the row ranges of 64 units per vector load and marks each
-// of its rows covered with one ballot per row, then the whole work group
-// clears the uncovered rows, 16 bytes per lane and store.
+// Zero the output rows that no unit covers, as a launch of its own (calls
+// with no unit to attend): kZeroRows rows per work group.
 constexpr int kZeroRows = 16;
 
 __global__ __launch_bounds__(256) void zero_uncovered_kernel(AttnParams p, int32_t row_bytes) {
     __shared__ uint32_t sTodo;
     const int32_t r0 = blockIdx.x * kZeroRows;
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        uint32_t cov = 0;                           // bit i: row r0 + i is covered
-        for (int32_t ub = 0; ub < p.num_units; ub += 64) {
-            const int32_t u = ub + lane;
-            int32_t q0 = 0, L = 0;
-            if (u < p.num_units) {
-                if (p.mode == kColumn) {
-                    q0 = p.seq_info[4 * (int64_t)u];
-                    L = p.seq_info[4 * (int64_t)u + 1];
-                } else if (p.mode == kPagedVarlen) {
-                    q0 = p.cu_seqlens_q[u];
-                    L = p.cu_seqlens_q[u + 1] - q0;
-                } else {
-                    q0 = u;
-                    L = 1;
-                }
-                if (L > p.max_seqlen_q) L = p.max_seqlen_q;
-            }
-#pragma unroll
-            for (int i = 0; i < kZeroRows; ++i) {
-                const int32_t r = r0 + i;
-                if (__ballot(r >= q0 && r - q0 < L) != 0) cov |= 1u << i;
-            }
-        }
-        if (lane == 0) {
-            const int32_t n = min(kZeroRows, p.total_q - r0);          // rows inside the output
-            const uint32_t inside = n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
-            sTodo = ~cov & inside;
-        }
-    }
-    __syncthreads();
-    const uint32_t todo = sTodo;
-    if (todo == 0) return;
-    const int32_t chunks = row_bytes / 16;
-    for (int32_t i = threadIdx.x; i < kZeroRows * chunks; i += 256) {
-        const int32_t rr = i / chunks, c = i - rr * chunks;
-        if ((todo >> rr) & 1u)
-            st16((uint8_t*)p.out + (int64_t)(r0 + rr) * row_bytes + (int64_t)c * 16, u32x4{0u, 0u, 0u, 0u});
-    }
+    const int32_t n = min(kZeroRows, p.total_q - r0);
+    zero_uncovered_rows(p, r0, n, row_bytes, &sTodo, 256);
 }
 
 int32_t vec_group_rows(int32_t group) {

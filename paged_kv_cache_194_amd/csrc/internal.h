@@ -54,6 +54,8 @@ struct AttnParams {
     int32_t vec_wgs;       // vector path: work-group slots per kv head
     int32_t vec_units;     // vector path: work items (units, or unit rows in row mode)
     int32_t row_mode;      // vector path takes each row of a unit as its own item
+    int32_t mfma_single;   // matrix-core path takes single-row units too (no vector launch)
+    int32_t zero_rows;     // the attention launch also zeroes the rows no unit covers
     float scale_log2;      // softmax_scale * log2(e)
 };
 
@@ -127,6 +129,68 @@ pkv_status decode_check(void* out, const void* q, const void* k_cache, const voi
                         int32_t max_seqlen_k, const void* k_new, const void* v_new,
                         int32_t q_heads, int32_t kv_heads, int32_t head_dim, float softmax_scale,
                         int32_t num_splits, pkv_dtype dtype, size_t* ws_bytes, size_t* ticket_bytes);
+
+// Zero the output rows [r0, r0 + n) (n <= 32) that no unit covers, run by a
+// whole work group of `nthreads` threads: wave 0 reads the units' row ranges
+// 64 per vector load and marks each covered row with one ballot, then every
+// thread clears uncovered rows 16 bytes at a time.  *todo is an LDS word.
+// Rows of a unit past max_seqlen_q count as uncovered.
+__device__ __forceinline__ void zero_uncovered_rows(const AttnParams& p, int32_t r0, int32_t n,
+                                                    int32_t row_bytes, uint32_t* todo, int nthreads) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        uint32_t cov = 0;                           // bit i: row r0 + i is covered
+        for (int32_t ub = 0; ub < p.num_units; ub += 64) {
+            const int32_t u = ub + lane;
+            int32_t q0 = 0, L = 0;
+            if (u < p.num_units) {
+                if (p.mode == kColumn) {
+                    q0 = p.seq_info[4 * (int64_t)u];
+                    L = p.seq_info[4 * (int64_t)u + 1];
+                } else if (p.mode == kPagedVarlen) {
+                    q0 = p.cu_seqlens_q[u];
+                    L = p.cu_seqlens_q[u + 1] - q0;
+                } else {
+                    q0 = u;
+                    L = 1;
+                }
+                if (L > p.max_seqlen_q) L = p.max_seqlen_q;
+            }
+            for (int i = 0; i < n; ++i) {
+                const int32_t r = r0 + i;
+                if (__ballot(r >= q0 && r - q0 < L) != 0) cov |= 1u << i;
+            }
+        }
+        if (lane == 0) {
+            const uint32_t inside = n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+            *todo = ~cov & inside;
+        }
+    }
+    __syncthreads();
+    const uint32_t t = *todo;
+    if (t == 0) return;
+    const int32_t chunks = row_bytes / 16;
+    for (int32_t i = threadIdx.x; i < n * chunks; i += nthreads) {
+        const int32_t rr = i / chunks, c = i - rr * chunks;
+        if ((t >> rr) & 1u)
+            *reinterpret_cast<uint4*>((uint8_t*)p.out + (int64_t)(r0 + rr) * row_bytes + (int64_t)c * 16) =
+                make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Uncovered-row zeroing inside an attention launch: the work groups of kv
+// head 0 (blockIdx.x == 0) each take an equal share of the rows, 32 at a
+// time, before their attention work (a separate column of work groups could
+// push a grid of one work group per CU into a second dispatch round).
+__device__ __forceinline__ void zero_rows_share(const AttnParams& p, int32_t row_bytes, uint32_t* todo,
+                                                int nthreads) {
+    const int64_t zi = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+    const int64_t nz = (int64_t)gridDim.y * gridDim.z;
+    const int64_t per = ((int64_t)p.total_q + nz - 1) / nz;
+    const int64_t end = (zi + 1) * per < p.total_q ? (zi + 1) * per : p.total_q;
+    for (int64_t r0 = zi * per; r0 < end; r0 += 32)
+        zero_uncovered_rows(p, (int32_t)r0, (int32_t)(end - r0 < 32 ? end - r0 : 32), row_bytes, todo, nthreads);
+}
 
 // Text for pkv_last_error() on the calling thread.
 void set_error(const char* fmt, ...);

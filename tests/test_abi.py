@@ -198,7 +198,10 @@ def test_split_choice_rules():
     """The library's own split counts (num_splits = 0).  One sequence: one work
     group per compute unit over its kv heads, at least 4 blocks (one per wave)
     per split.  Several sequences: about 2048 work groups, at least 8 blocks per
-    split.  A call that holds multi-row units caps the vector path at 4."""
+    split.  A call that may hold multi-row units runs on the matrix cores only:
+    about one dispatch round of work groups (CUs x work groups per CU, 1 at
+    head_dim 256 and 2 below) over the (unit, row tile) items, at least 8 chunks
+    per split."""
     import torch
     if torch.cuda.is_available():
         cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -212,6 +215,8 @@ def test_split_choice_rules():
     assert one(8192, hkv=2) == min(cus // 2, 8192 // 16 // 4)
     assert pkv.attn_num_splits(64, 1, 8192, 32, 8, 128, 0) == 4           # 2048 / (64 * 8)
     assert pkv.attn_num_splits(4, 1, 65536, 64, 8, 256, 0) == 64           # 2048 / (4 * 8)
-    assert pkv.attn_num_splits(4, 16, 65536, 64, 8, 256, 0) == 4           # multi-row units: capped
-    assert pkv.attn_num_splits(32, 512, 16384, 32, 8, 128, 0) == 4
+    # matrix cores: 4 units x 8 kv heads x 1 row tile (16 rows x 8 heads = 128) = 32 items
+    assert pkv.attn_num_splits(4, 16, 65536, 64, 8, 256, 0) == (cus + 16) // 32
+    # 32 units x 8 kv heads x 16 row tiles (512 rows x 4 heads / 128) = 4096 items: one split
+    assert pkv.attn_num_splits(32, 512, 16384, 32, 8, 128, 0) == 1
     assert pkv.attn_num_splits(32, 512, 16384, 32, 8, 128, 6) == 6         # an explicit count is kept

@@ -268,9 +268,10 @@ def test_nonfinite_value_in_hidden_live_key():
 
 
 def test_mfma_tickets_back_to_zero():
-    """The matrix-core path's split-K arrival counters (after the vector path's
-    in the workspace) all read 0 after every call, so one workspace serves calls
-    of different split counts."""
+    """The matrix-core path's split-K arrival counters (at the start of the
+    workspace: a call that may hold multi-row units launches no vector kernel)
+    all read 0 after every call, so one workspace serves calls of different
+    split counts."""
     inp = workloads.paged_inputs(seed=79, lengths=[700, 300, 1500], q_lens=[16, 40, 64], q_heads=32,
                                  kv_heads=8, head_dim=128, dtype=torch.bfloat16, num_blocks=200,
                                  max_blocks=100, causal=True, device=DEV)
@@ -278,8 +279,7 @@ def test_mfma_tickets_back_to_zero():
     ws = torch.zeros(pkv.attn_workspace_bytes(3, 64, inp.max_seqlen_k, 32, 8, 128, 64), dtype=torch.uint8,
                      device=DEV)
     tiles = (64 * 4 + 127) // 128
-    vec_tickets = 3 * 8 * 256
-    mfma = ws[vec_tickets:vec_tickets + 3 * tiles * 8 * 256].view(torch.int32)[::64]
+    mfma = ws[:3 * tiles * 8 * 256].view(torch.int32)[::64]
     for s in (5, 64, 2, 5):
         out = torch.full_like(inp.q, float("nan"))
         pkv.varlen_attn(out, inp.q, inp.k_cache, inp.v_cache, cu_seqlens_q=inp.cu_seqlens_q,
@@ -288,4 +288,4 @@ def test_mfma_tickets_back_to_zero():
                         workspace=ws)
         torch.cuda.synchronize()
         check_close(out, ref, "bf16", f"splits={s}")
-        assert int(mfma.abs().sum()) == 0 and int(ws[:vec_tickets].view(torch.int32).abs().sum()) == 0, s
+        assert int(mfma.abs().sum()) == 0, (s, mfma.tolist())
