@@ -44,7 +44,14 @@ METRIC = "decode attention KV GB/s (% of HBM peak) + µs/step at 4K ctx, 1×MI35
 TRAFFIC_SOURCES = {
     "decode_step_4k": ["attn_vec.hip", "device_util.h", "internal.h", "api.hip"],
     "prefix_import_4k": ["prefix_copy.hip", "device_util.h", "internal.h", "api.hip"],
+    "batched64": ["attn_vec.hip", "device_util.h", "internal.h", "api.hip"],
+    "long_decode_d256": ["attn_vec.hip", "device_util.h", "internal.h", "api.hip"],
+    "column_store": ["attn_mfma.hip", "device_util.h", "internal.h", "api.hip"],
+    "draft_verify_d256": ["attn_mfma.hip", "device_util.h", "internal.h", "api.hip"],
 }
+# bench --config of each traffic record
+TRAFFIC_KEY = {"c2": "decode_step_4k", "prefix": "prefix_import_4k", "c3": "batched64",
+               "c5d": "long_decode_d256", "c4": "column_store", "c5": "draft_verify_d256"}
 
 
 def kernel_source_hash(workload: str) -> str:
@@ -56,18 +63,24 @@ def kernel_source_hash(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per launch from committed PMC summaries, if they were taken on
-    the current sources of the workload's kernel; else None."""
+def profile_record(workload: str) -> dict:
+    """The committed PMC record of the workload's dominant kernel, if it was
+    taken on the current sources of that kernel; else {}."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         data = json.load(f)
     rec = data.get(workload)
     if not rec or rec.get("kernel_source_sha") != kernel_source_hash(workload):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return {}
+    return rec
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from committed PMC summaries, if they were taken on
+    the current sources of the workload's kernel; else None."""
+    return profile_record(workload).get("hbm_bytes_per_launch")
 
 
 def cpu_threads() -> int:
@@ -286,6 +299,24 @@ def cpu_baseline_decode(args, torch, cache, inputs, L, kv_bytes_step):
 # One-call workloads: batched paged decode, column store, long context
 # ---------------------------------------------------------------------------
 
+def host_bits(torch, t):
+    """A device tensor's raw bits on the host (bf16 as uint16), as the oracle takes them."""
+    import numpy as np
+    h = t.cpu()
+    return h.view(torch.int16).numpy().view(np.uint16) if h.dtype == torch.bfloat16 else h.numpy()
+
+
+def cpu_baseline_call(run, fraction: float, kv_bytes: int, sample: str) -> dict:
+    """The oracle, as it stands, on the same bits: ``run()`` computes the
+    sampled part of the call, ``fraction`` is that part's share of the call's
+    work (visible query-key pairs), and the time is scaled to the whole call."""
+    t0 = time.perf_counter()
+    run()
+    sec = (time.perf_counter() - t0) / fraction
+    return {"value": round(kv_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle", "sec_per_call": round(sec, 3), **host_info(), "sample": sample}
+
+
 def bench_single_call(args, torch):
     import numpy as np
 
@@ -308,6 +339,14 @@ def bench_single_call(args, torch):
                                   num_splits=args.splits, workspace=ws)
         name = "batched paged decode, 64 sequences, lengths U[1,8192], 40000-block pool"
         extra = {"sum_len": int(used.sum())}
+
+        def oracle_run():
+            import oracle
+            oracle.paged_attention(host_bits(torch, inp.q), host_bits(torch, inp.k_cache),
+                                   host_bits(torch, inp.v_cache), inp.block_table.cpu().numpy(),
+                                   inp.cu_seqlens_q.cpu().numpy(), used, dtype="bf16", scale=inp.scale,
+                                   max_seqlen_k=inp.max_seqlen_k)
+        oracle_fraction, oracle_sample = 1.0, "all 64 sequences (host copies of the inputs included)"
     elif args.config == "c5d":
         inp = workloads.c5_long(device=dev, decode=True)
         used = inp.seqused_k.cpu().numpy().astype(np.int64)
@@ -324,19 +363,34 @@ def bench_single_call(args, torch):
                                   num_splits=splits, workspace=ws)
         name = "long-context decode, 4 sequences 32K/64K, 64 q / 8 kv heads, D 256, 16 splits"
         extra = {}
+
+        def oracle_run():
+            import oracle
+            oracle.paged_attention(host_bits(torch, inp.q), host_bits(torch, inp.k_cache),
+                                   host_bits(torch, inp.v_cache), inp.block_table.cpu().numpy(),
+                                   inp.cu_seqlens_q.cpu().numpy(), used, dtype="bf16", scale=inp.scale,
+                                   causal=True, max_seqlen_k=inp.max_seqlen_k, seqs=[0, 1])
+        oracle_fraction = float(used[:2].sum()) / float(used.sum())
+        oracle_sample = (f"sequences 0 and 1 ({int(used[0])} + {int(used[1])} keys) of 4, scaled by "
+                         "live keys (host copies of the inputs included)")
     elif args.config in ("c4", "c5"):
         return bench_multirow(args, torch)
     else:
         raise SystemExit(f"unknown --config {args.config}")
     sec = time_call(torch, call, args)
     gbs = kv_bytes / sec / 1e9
-    return {"metric": f"{name}: KV GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
-            "us_per_call": round(sec * 1e6, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic", "config": {"workload": name, "kv_bytes": kv_bytes, **extra},
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+    res = {"metric": f"{name}: KV GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+           "us_per_call": round(sec * 1e6, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": name, "kv_bytes": kv_bytes, **extra},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": traffic_from_profiles(TRAFFIC_KEY[args.config]),
+                        "bytes_per_launch": kv_bytes}}
+    if not args.no_cpu_baseline and not args.eager:
+        res["cpu_baseline"] = cpu_baseline_call(oracle_run, oracle_fraction, kv_bytes, oracle_sample)
+    return res
 
 
 def bench_prefix(args, torch):
@@ -487,6 +541,13 @@ def bench_multirow(args, torch):
                             max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=mk, softmax_scale=inp.scale,
                             causal=True, window=window, num_splits=args.splits, workspace=ws)
         name = "column store [8192,32,8,128]: 24 decode + 8 chunked-prefill segments, causal, window 4096"
+
+        def oracle_run():
+            import oracle
+            oracle.column_attention(host_bits(torch, inp.q), host_bits(torch, inp.k_store),
+                                    host_bits(torch, inp.v_store), info, dtype="bf16", scale=inp.scale,
+                                    causal=True, window=window, max_seqlen_q=inp.max_seqlen_q)
+        oracle_seqs = None
     else:
         inp = workloads.c5_long(device=dev)
         used = inp.seqused_k.cpu().numpy()
@@ -503,28 +564,51 @@ def bench_multirow(args, torch):
                             max_seqlen_k=inp.max_seqlen_k, softmax_scale=inp.scale, causal=False,
                             num_splits=args.splits, workspace=ws)
         name = "long-context draft verify: 4 x 16-token blocks over 32K/64K keys, 64 q / 8 kv heads, D 256"
-    keys = pairs = 0
-    for L, E in units:
+
+        def oracle_run():
+            import oracle
+            oracle.paged_attention(host_bits(torch, inp.q), host_bits(torch, inp.k_cache),
+                                   host_bits(torch, inp.v_cache), inp.block_table.cpu().numpy(),
+                                   inp.cu_seqlens_q.cpu().numpy(), used, dtype="bf16", scale=inp.scale,
+                                   causal=False, max_seqlen_q=16, max_seqlen_k=inp.max_seqlen_k,
+                                   seqs=[0, 1])
+        oracle_seqs = [0, 1]
+    keys = pairs = sample_pairs = 0
+    for u, (L, E) in enumerate(units):
         k_u, p_u = visible_pairs(E, L, causal, window)
         keys += k_u
         pairs += p_u
+        if oracle_seqs is None or u in oracle_seqs:
+            sample_pairs += p_u
     kv_bytes = keys * inp.kv_heads * inp.head_dim * 2 * 2
     flops = 4 * inp.head_dim * inp.q_heads * pairs
     sec = time_call(torch, call, args)
     gbs, tfs = kv_bytes / sec / 1e9, flops / sec / 1e12
     hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tfs / 2500.0
     bound = "hbm" if kv_bytes / (HBM_PEAK_GBS * 1e9) >= flops / 2.5e15 else "mfma"
+    prof = profile_record(TRAFFIC_KEY[args.config])
     roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-             "frac": round(hbm_frac, 4), "traffic": None} if bound == "hbm" else
+             "frac": round(hbm_frac, 4)} if bound == "hbm" else
             {"bound": "mfma", "achieved": round(tfs, 2), "peak": 2500.0, "unit": "TFLOP/s",
-             "frac": round(mfma_frac, 4), "traffic": None})
-    return {"metric": f"{name}: KV GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
-            "us_per_call": round(sec * 1e6, 2), "pct_hbm_peak": round(100 * hbm_frac, 2),
-            "tflops": round(tfs, 2), "pct_mfma_peak": round(100 * mfma_frac, 2),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic", "config": {"workload": name, "kv_bytes": kv_bytes, "flops": flops},
-            "roofline": roof}
+             "frac": round(mfma_frac, 4)})
+    roof.update({"traffic": prof.get("hbm_bytes_per_launch"), "bytes_per_launch": kv_bytes,
+                 "flops_per_launch": flops,
+                 # busy cycles of every MFMA issued (masked keys included) over the
+                 # kernel's SIMD-cycles, from the committed counter record
+                 "mfma_busy_pct": prof.get("mfma_busy_pct")})
+    res = {"metric": f"{name}: KV GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+           "us_per_call": round(sec * 1e6, 2), "pct_hbm_peak": round(100 * hbm_frac, 2),
+           "tflops": round(tfs, 2), "pct_mfma_peak": round(100 * mfma_frac, 2),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": name, "kv_bytes": kv_bytes, "flops": flops},
+           "roofline": roof}
+    if not args.no_cpu_baseline and not args.eager:
+        sample = ("all 32 segments" if oracle_seqs is None else
+                  f"sequences {oracle_seqs} of {len(units)}, scaled by visible query-key pairs")
+        res["cpu_baseline"] = cpu_baseline_call(oracle_run, sample_pairs / pairs, kv_bytes,
+                                                sample + " (host copies of the inputs included)")
+    return res
 
 
 def main():
