@@ -182,6 +182,8 @@ template <int D, int NW, int RT, int BN, int NS, int WPE, bool PAGED>
 __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     using C = MfmaCfg<D, NW, RT, BN, NS>;
     constexpr bool kMfmaPrio = D <= 128;
+    constexpr bool kRot = NW >= 8;                // two wave groups one phase apart (see the chunk loop)
+    static_assert(!kRot || NS >= 4, "the second wave group keeps a chunk's V one step longer");
     constexpr int NT = C::NT, BM = C::BM, RB = C::RB, RC = C::RC, CB = C::CB, IPW = C::IPW,
                   KT = C::KT, KS = C::KS, DT = C::DT;
 
@@ -412,19 +414,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
         }
     };
 
-    auto compute = [&](int32_t c, int st_idx, const uint8_t* sKb, const uint8_t* sVb) __attribute__((always_inline)) {
-        if (wave_idle) return;
-        const int32_t c0 = c_base + c * BN;
-        const uint32_t bad = (nostore >> (KT * st_idx)) & ((1u << KT) - 1u);   // tiles without storage
-        // A wave issues its two MFMA passes at raised priority and its softmax at
-        // the normal one, so that on a SIMD shared with a wave of another phase
-        // the matrix core is fed first and the VALU work fills the gaps (the
-        // per-chunk barrier otherwise keeps a work group's waves in step).
-        // Column-store step with head_dim 128: 437 -> 411 us; not taken at
-        // head_dim 256, where it measured no gain.
+    // A wave issues its two MFMA passes at raised priority and its softmax at
+    // the normal one, so that on a SIMD shared with a wave of another phase
+    // the matrix core is fed first and the VALU work fills the gaps (the
+    // per-chunk barrier otherwise keeps a work group's waves in step).
+    // Column-store step with head_dim 128: 437 -> 411 us; not taken at
+    // head_dim 256, where it measured no gain.
+    // ---- S^T = K . Q^T for this wave's RT x 16 rows and one chunk's BN keys ----
+    auto qk = [&](const uint8_t* sKb, f32x4_t (&st)[RT][KT]) __attribute__((always_inline)) {
         if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(1);
-        // ---- S^T = K . Q^T for this wave's RT x 16 rows and the chunk's BN keys ----
-        f32x4_t st[RT][KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -438,6 +436,12 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             }
         }
         if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(0);
+    };
+    // ---- online softmax of chunk c's scores st, then O^T += V^T . P^T ----
+    auto softmax_pv = [&](int32_t c, int st_idx, const f32x4_t (&st)[RT][KT], const uint8_t* sVb)
+        __attribute__((always_inline)) {
+        const int32_t c0 = c_base + c * BN;
+        const uint32_t bad = (nostore >> (KT * st_idx)) & ((1u << KT) - 1u);   // tiles without storage
         // ---- online softmax (row lr of tile rt; keys kt*16 + 4*lq + e) ----
         // A chunk inside every row's visible range (the common case) needs no
         // per-key mask: a wave-uniform test picks that path.  Rows past M are
@@ -539,7 +543,50 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     // Loads past the range read the zero row, so every step waits for the
     // same count.
     const int32_t n = c_end > c_first ? c_end - c_first : 0;
-    if (n > 0) {
+    if constexpr (kRot) {
+      if (n > 0) {
+        // Eight waves, two to a SIMD: waves 0..3 run each chunk's scores,
+        // softmax and PV in the step the chunk lands; waves 4..7 (the other
+        // wave of every SIMD) run the softmax and PV of the chunk before, then
+        // the scores of this one, so that on each SIMD one wave's exponentials
+        // meet the other's products instead of the same phase.  A chunk's V is
+        // read one step later by the second group, so loads run NS - 2 chunks
+        // ahead: step i waits for chunk i, barrier, issues chunk i + NS - 2
+        // into the stage of chunk i - 2, computes.  Step n only finishes the
+        // second group's last chunk.
+        const bool late = wave >= NW / 2;
+#pragma unroll
+        for (int s = 0; s < NS - 2; ++s) {
+            if (s < n) ensure_ids(c_first + s);
+            issue(c_first + s, s);
+        }
+        f32x4_t sprev[RT][KT];                    // second group: scores of the chunk before
+        for (int32_t i = 0; i <= n; ++i) {
+            wait_vm<2 * IPW * (NS - 3)>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (i + NS - 2 < n) ensure_ids(c_first + i + NS - 2);
+            issue(c_first + i + NS - 2, (i + NS - 2) % NS);
+            if (!wave_idle) {
+                const int st = i % NS;
+                if (!late) {
+                    if (i < n) {
+                        f32x4_t sc4[RT][KT];
+                        qk(&sKV[st][0], sc4);
+                        softmax_pv(c_first + i, st, sc4, &sKV[st][CB]);
+                    }
+                } else {
+                    if (i > 0) {
+                        const int sp = (i - 1) % NS;
+                        softmax_pv(c_first + i - 1, sp, sprev, &sKV[sp][CB]);
+                    }
+                    if (i < n) qk(&sKV[st][0], sprev);
+                }
+            }
+        }
+        wait_vm<0>();                             // no load may land after the work group ends
+      }
+    } else if (n > 0) {
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s) {
             if (s < n) ensure_ids(c_first + s);
@@ -552,7 +599,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             if (i + NS - 1 < n) ensure_ids(c_first + i + NS - 1);
             issue(c_first + i + NS - 1, (i + NS - 1) % NS);
             const int st = i % NS;
-            compute(c_first + i, st, &sKV[st][0], &sKV[st][CB]);
+            if (!wave_idle) {
+                f32x4_t sc4[RT][KT];
+                qk(&sKV[st][0], sc4);
+                softmax_pv(c_first + i, st, sc4, &sKV[st][CB]);
+            }
         }
         wait_vm<0>();                             // no load may land after the work group ends
     }
