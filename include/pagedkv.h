@@ -122,10 +122,10 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  *                the call first appends them at position seqused_k[b] - 1 of
  *                each sequence (the slot found through block_table; nothing for
  *                an empty sequence or an entry outside the pool) and then
- *                attends, as one step: inside the attention kernel for
- *                q_heads / kv_heads <= 8, as a launch of its own before the
- *                matrix-core attention above that.  When NULL the cache is only
- *                read.
+ *                attends, as one step: inside the attention kernel on the
+ *                vector path, as a launch of its own before the attention on
+ *                the matrix-core path (bf16 with q_heads / kv_heads >= 8).
+ *                When NULL the cache is only read.
  * softmax_scale: multiplies q.k before the softmax.
  * causal       : with one query per sequence causal equals non-causal.
  * window       : > 0 keeps the last `window` keys (p - window + 1 .. p).
@@ -143,8 +143,9 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, int64_t num_slots,
  *                takes more of them.  Results of different split counts agree to
  *                rounding; the same inputs and split count give the same bits.
  *                The library's own choice depends on the current device's
- *                compute-unit count for a single sequence and for multi-row
- *                units.
+ *                compute-unit count.  On the matrix-core path (bf16, groups of
+ *                8 and above) the num_splits * num_seqs work groups of a kv
+ *                head are dealt the same way over the sequences.
  * workspace    : device scratch of at least pkv_attn_workspace_bytes(num_seqs, 1,
  *                max_seqlen_k, q_heads, kv_heads, head_dim, num_splits) bytes
  *                (may be NULL when that is 0).  It starts with split-K arrival
@@ -196,10 +197,11 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q,
  * Other arguments as for pkv_paged_decode_attn.  workspace must hold
  * pkv_attn_workspace_bytes(units, max_seqlen_q, ...) bytes with units =
  * num_seqs or num_segments.
- * Kernels: bf16 units of one query row (and GQA groups <= 8) run on the vector
- * path, bf16 units of several rows (or groups > 8) on the matrix cores; fp32
- * takes every covered query row as a single query on the vector path (fp32
- * products throughout), groups <= 8 only (PKV_EUNSUPPORTED above).
+ * Kernels: bf16 calls with max_seqlen_q = 1 and GQA groups below 8 run on the
+ * vector path; bf16 calls that may hold units of several rows, or with groups
+ * of 8 and above, on the matrix cores; fp32 takes every covered query row as a
+ * single query on the vector path (fp32 products throughout), groups <= 8
+ * only (PKV_EUNSUPPORTED above).
  */
 pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q,
                            const void* k, const void* v,
@@ -374,15 +376,16 @@ pkv_status pkv_paged_decode_attn_noalloc(void* out, const void* q,
  * arguments needs (split-K partials); 0 when it needs none.  `units` is num_seqs
  * (paged) or num_segments (column); num_splits as passed to the call.  With
  * num_splits = 0 the answer depends on the current device (its compute-unit
- * count), so ask with the device current that will run the call.
+ * count), so ask with the device current that will run the call.  The size
+ * covers bf16 and fp32 calls alike.
  */
 size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                 int32_t num_splits);
 
-/* Split count the library uses for these host arguments (num_splits = 0 picks):
- * the vector path's for calls of single-row units with groups <= 8, else the
- * matrix-core path's. */
+/* Split count the library uses for a bf16 call with these host arguments
+ * (num_splits = 0 picks): the vector path's for calls of single-row units with
+ * groups below 8, else the matrix-core path's. */
 int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seqlen_k,
                             int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                             int32_t num_splits);

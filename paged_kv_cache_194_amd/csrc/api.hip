@@ -76,10 +76,15 @@ int32_t device_cus() {
     return n;
 }
 
-// Vector path.  Several units: about 2048 work groups (four dispatch rounds
-// at two per CU; the balanced deal keeps them even; the 64-sequence batch
-// measured 207 us against 214 us at 1024), at least 8 blocks (two per wave)
-// per split.  One unit: one work group per CU -- a single short round in which
+// Vector path.  Several units: about one dispatch round of work groups (two
+// per CU), and at least 4 splits per unit so that the balanced deal can even
+// out unequal lengths; at least 8 blocks (two per wave) per split.  Each work
+// group pays a fixed cost (the deal, the start of its stream, the split-K
+// hand-off) of several microseconds under a full stream, so more rounds of
+// smaller pieces lose: 2 sequences of 16K/4K keys (D 128) 31 us at 16 splits
+// against 63 us at 128; 4 of 32K/64K 145 us at 16 against 167 us at 64; 16
+// of up to 8K (D 256) 96-101 us at 2-4 against 156 us at 16; 64 of up to
+// 8K (D 128) 197-200 us at 2-4 splits, 215 us at 8.  One unit: one work group per CU -- a single short round in which
 // every split's work group is on the critical path, each wave with the same
 // number of blocks where the length allows (the 4096-key, 8-head decode step
 // measured 434 us at 32 splits, 448 us at 24, 456 us at 28, 504 us at 36) --
@@ -90,9 +95,11 @@ int32_t pick_splits(int32_t units, int32_t kv_heads, int32_t keys, int32_t num_s
     if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
     const int64_t base = (int64_t)(units > 0 ? units : 1) * kv_heads;
     const int64_t blocks = ((int64_t)(keys > 0 ? keys : 1) + 15) / 16;
-    const int64_t target = units <= 1 ? (int64_t)device_cus() : 2048;
     const int64_t per = units <= 1 ? 4 : 8;         // blocks per split at least
-    return clamp_splits((target + base - 1) / base, blocks / per > 0 ? blocks / per : 1);
+    if (units <= 1)
+        return clamp_splits(((int64_t)device_cus() + base - 1) / base, blocks / per > 0 ? blocks / per : 1);
+    const int64_t s = (2 * (int64_t)device_cus() + base / 2) / base;
+    return clamp_splits(s > 4 ? s : 4, blocks / per > 0 ? blocks / per : 1);
 }
 
 // Plan of one attention call: which paths run, their split counts and the
@@ -110,7 +117,7 @@ struct Plan {
 };
 
 Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_heads, int32_t kv_heads,
-               int32_t head_dim, int32_t num_splits) {
+               int32_t head_dim, int32_t num_splits, bool mfma_ok) {
     Plan pl{};
     const int32_t group = q_heads / kv_heads;
     const int32_t U = units > 0 ? units : 1;
@@ -118,8 +125,18 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
     // matrix cores, single-row ones included, in one launch: which units have
     // one row only the device knows, and a separate vector launch would run
     // after, not beside, the matrix-core one.
-    pl.vec = group <= kVecMaxGroup && max_seqlen_q <= 1;
-    pl.mfma = max_seqlen_q > 1 || group > kVecMaxGroup;
+    // Single-row units with a GQA group of 8 also run on the matrix cores
+    // where they can (bf16): the vector kernel holds one wave per SIMD there
+    // (377 VGPRs at head_dim 256), while the matrix-core kernel streams the
+    // chunks through LDS with eight rows of a 16-row tile live.  Same inputs,
+    // same box: 4 sequences of 32K/64K keys, D 256, 333 against 389-515 us;
+    // D 128, 195 against 295 us; 16 sequences of up to 8K, D 128, 64 against
+    // 152 us; 64 sequences of up to 8K, D 256, 563 against 595 us.  Groups of
+    // 4 and below stay on the vector kernel (D 128, 64 sequences: 198 against
+    // 325 us).
+    const bool g8_mfma = mfma_ok && group >= kVecMaxGroup;
+    pl.vec = group <= kVecMaxGroup && max_seqlen_q <= 1 && !g8_mfma;
+    pl.mfma = max_seqlen_q > 1 || group > kVecMaxGroup || g8_mfma;
     pl.splits = pick_splits(units, kv_heads, keys, num_splits);
     pl.gt = pkv::vec_group_rows(group);
     if (pl.vec && pl.splits > 1) {
@@ -324,11 +341,16 @@ size_t pkv_attn_workspace_bytes(int32_t units, int32_t max_seqlen_q, int32_t max
                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                 int32_t num_splits) {
     if (units <= 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || head_dim <= 0) return 0;
-    size_t need = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).ws_bytes;
-    // An fp32 call with several rows per unit runs in row mode: cover that plan too.
+    // The plan depends on the dtype (bf16 may take the matrix cores, fp32 the
+    // vector path, row by row for several rows per unit): cover every plan.
+    size_t need = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits, true).ws_bytes;
+    const size_t vec_need =
+        make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits, false).ws_bytes;
+    if (vec_need > need) need = vec_need;
     const int64_t items = row_items(units, max_seqlen_q);
     if (max_seqlen_q > 1 && q_heads / kv_heads <= kVecMaxGroup && items <= INT32_MAX) {
-        const size_t rows = make_plan((int32_t)items, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits).ws_bytes;
+        const size_t rows =
+            make_plan((int32_t)items, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits, false).ws_bytes;
         if (rows > need) need = rows;
     }
     return need;
@@ -338,7 +360,8 @@ int32_t pkv_attn_num_splits(int32_t units, int32_t max_seqlen_q, int32_t max_seq
                             int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                             int32_t num_splits) {
     if (kv_heads <= 0) return 1;
-    const Plan pl = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    // As a bf16 call would split (head_dim 64/128/256).
+    const Plan pl = make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits, true);
     return pl.vec ? pl.splits : pl.msplits;
 }
 
@@ -369,7 +392,8 @@ pkv_status decode_check(void* out, const void* q, const void* k_cache, const voi
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !seqused_k)
         return fail(PKV_EINVAL, "null pointer argument");
-    const Plan pl = make_plan(num_seqs, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    const Plan pl = make_plan(num_seqs, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits,
+                              pkv::attn_mfma_supported(dtype, head_dim));
     *ws_bytes = pl.ws_bytes;
     *ticket_bytes = plan_ticket_bytes(pl);
     return PKV_OK;
@@ -397,15 +421,16 @@ pkv_status pkv_paged_decode_attn(void* out, const void* q, const void* k_cache, 
     if (num_seqs == 0) return ok();
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-    const Plan pl = make_plan(num_seqs, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+    const Plan pl = make_plan(num_seqs, 1, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits,
+                              pkv::attn_mfma_supported(dtype, head_dim));
     const int32_t group = q_heads / kv_heads;
 
     const int64_t cap64 = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
     const int32_t kv_cap = (int32_t)(cap64 < max_seqlen_k ? cap64 : max_seqlen_k);
     hipStream_t st = (hipStream_t)stream;
     pkv::AttnParams p{};
-    // The vector kernel appends inside the attention; a group above 8 runs on
-    // the matrix cores, so the append goes first as its own launch.
+    // The vector kernel appends inside the attention; on the matrix-core path
+    // (bf16 groups of 8 and above) the append goes first as its own launch.
     const bool append_first = k_new && !pl.vec;
     if (append_first) {
         pkv_status s2 = hip_status(
@@ -488,8 +513,9 @@ pkv_status pkv_varlen_attn(void* out, const void* q, int32_t total_q, const void
     if (total_q == 0) return ok();
     if (!out || !q || !k || !v) return fail(PKV_EINVAL, "null pointer argument");
     const Plan pl = row_mode ? make_plan((int32_t)row_items(units, max_seqlen_q), 1, max_seqlen_k, q_heads, kv_heads,
-                                         head_dim, num_splits)
-                             : make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits);
+                                         head_dim, num_splits, false)
+                             : make_plan(units, max_seqlen_q, max_seqlen_k, q_heads, kv_heads, head_dim, num_splits,
+                                         pkv::attn_mfma_supported(dtype, head_dim));
     if (workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !workspace))
         return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.ws_bytes);
 

@@ -195,13 +195,14 @@ def test_split_choice_is_static_and_bounded():
 
 
 def test_split_choice_rules():
-    """The library's own split counts (num_splits = 0).  One sequence: one work
-    group per compute unit over its kv heads, at least 4 blocks (one per wave)
-    per split.  Several sequences: about 2048 work groups, at least 8 blocks per
-    split.  A call that may hold multi-row units runs on the matrix cores only:
-    about one dispatch round of work groups (CUs x work groups per CU, 1 at
-    head_dim 256 and 2 below) over the (unit, row tile) items, at least 8 chunks
-    per split."""
+    """The library's own split counts (num_splits = 0), as a bf16 call takes them.
+    One sequence: one work group per compute unit over its kv heads, at least 4
+    blocks (one per wave) per split.  Several sequences on the vector path
+    (groups up to 4): about one round of work groups (two per CU), at least 4
+    splits per unit and 8 blocks per split.  Groups of 8 and above, and calls
+    that may hold multi-row units, run on the matrix cores: about one dispatch
+    round of work groups (CUs x work groups per CU, 1 at head_dim 256 and 2
+    below) over the (unit, row tile) items, at least 8 chunks per split."""
     import torch
     if torch.cuda.is_available():
         cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -213,8 +214,11 @@ def test_split_choice_rules():
     assert one(512) == min(cus // 8, 512 // 16 // 4)
     assert one(64) == 1
     assert one(8192, hkv=2) == min(cus // 2, 8192 // 16 // 4)
-    assert pkv.attn_num_splits(64, 1, 8192, 32, 8, 128, 0) == 4           # 2048 / (64 * 8)
-    assert pkv.attn_num_splits(4, 1, 65536, 64, 8, 256, 0) == 64           # 2048 / (4 * 8)
+    assert pkv.attn_num_splits(64, 1, 8192, 32, 8, 128, 0) == 4           # at least 4
+    assert pkv.attn_num_splits(4, 1, 65536, 32, 8, 128, 0) == max(4, (2 * cus + 16) // 32)
+    assert pkv.attn_num_splits(2, 1, 16384, 32, 8, 128, 0) == max(4, (2 * cus + 8) // 16)
+    # group 8 on the matrix cores: 4 units x 8 kv heads x 1 row tile = 32 items
+    assert pkv.attn_num_splits(4, 1, 65536, 64, 8, 256, 0) == (cus + 16) // 32
     # matrix cores: 4 units x 8 kv heads x 1 row tile (16 rows x 8 heads = 128) = 32 items
     assert pkv.attn_num_splits(4, 16, 65536, 64, 8, 256, 0) == (cus + 16) // 32
     # 32 units x 8 kv heads x 16 row tiles (512 rows x 4 heads / 128) = 4096 items: one split
