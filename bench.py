@@ -45,7 +45,7 @@ TRAFFIC_SOURCES = {
     "decode_step_4k": ["attn_vec.hip", "device_util.h", "internal.h", "api.hip"],
     "prefix_import_4k": ["prefix_copy.hip", "device_util.h", "internal.h", "api.hip"],
     "batched64": ["attn_vec.hip", "device_util.h", "internal.h", "api.hip"],
-    "long_decode_d256": ["attn_vec.hip", "device_util.h", "internal.h", "api.hip"],
+    "long_decode_d256": ["attn_mfma.hip", "device_util.h", "internal.h", "api.hip"],
     "column_store": ["attn_mfma.hip", "device_util.h", "internal.h", "api.hip"],
     "draft_verify_d256": ["attn_mfma.hip", "device_util.h", "internal.h", "api.hip"],
 }
