@@ -193,7 +193,7 @@ pkv_status run_attention(pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim, 
         return fail(PKV_EUNSUPPORTED, "%d vector-path work groups per kv head exceed the grid limit: pass a "
                     "smaller num_splits", p.vec_wgs);
     if (pl.mfma && p.num_units > 0 &&
-        (int64_t)pl.tiles * pl.msplits * (pl.msplits > 1 && (int64_t)p.num_units * pl.tiles > 1 ? p.num_units : 1) >
+        (int64_t)pl.tiles * pl.msplits * (pl.msplits > 1 ? p.num_units : 1) >
             kMaxGridY)
         return fail(PKV_EUNSUPPORTED, "too many matrix-core work groups per kv head: pass a smaller num_splits");
     char* partials = ws + plan_ticket_bytes(pl);

@@ -204,18 +204,19 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     const int lr = lane & 15;                     // this lane's query row within the wave
     const int lq = lane >> 4;                     // lane group 0..3
 
-    // Work items are (unit, row tile).  With one split, or one item, slot
-    // blockIdx.y of unit blockIdx.z is (tile, split).  Otherwise the
-    // mfma_splits * items slots of a kv head are dealt over the items: an item
-    // of n chunks gets max(1, ceil(n / c)) consecutive slots, c the smallest
-    // chunk count per slot for which the deal fits the grid.
+    // Work items are (unit, row tile).  With one split, slot blockIdx.y of
+    // unit blockIdx.z is row tile blockIdx.y.  With several, the
+    // mfma_splits * items slots of a kv head are dealt over the items (a call
+    // of one item included): an item of n chunks gets max(1, ceil(n / c))
+    // consecutive slots, c the smallest chunk count per slot for which the
+    // deal fits the grid.
     int32_t u, tile, split, S, slot0;
-    if (p.mfma_splits == 1 || p.num_units * T == 1) {
-        S = p.mfma_splits;
-        tile = blockIdx.y / S;
-        split = blockIdx.y - tile * S;
+    if (p.mfma_splits == 1) {
+        S = 1;
+        tile = blockIdx.y;
+        split = 0;
         u = blockIdx.z;
-        slot0 = (u * T + tile) * S;
+        slot0 = u * T + tile;
     } else {
         if (wave == 0) {
             const int32_t NI = p.num_units * T;
@@ -727,7 +728,7 @@ bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim) {
 template <int D>
 static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
     using Sh = MfmaShape<D>;
-    const bool dealt = p.mfma_splits > 1 && p.num_units * p.mfma_tiles > 1;
+    const bool dealt = p.mfma_splits > 1;
     dim3 grid(p.kv_heads, p.mfma_tiles * p.mfma_splits * (dealt ? p.num_units : 1), dealt ? 1 : p.num_units);
     if (p.mode == kColumn) {
         attn_mfma_kernel<D, Sh::NW, Sh::RT, Sh::BN, Sh::NS, Sh::WPE, false><<<grid, dim3(64 * Sh::NW), 0, stream>>>(p);

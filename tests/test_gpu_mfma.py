@@ -131,6 +131,23 @@ def test_large_group_decode_through_mfma():
         check_close(out, ref, "bf16", f"G=16 splits={s}")
 
 
+@pytest.mark.skip(reason="one-sequence calls with several splits on the matrix-core path: a timing run of "
+                         "this shape (4096 keys, D 128, G 4 and 8, max_seqlen_q 2, 8-64 splits, with the "
+                         "vector path's one-sequence varlen calls before it) ended in a GPU memory fault "
+                         "whose cause reading has not found; such calls now take the dealt assignment the "
+                         "multi-unit tests run, and stay off the GPU until the cause is shown")
+def test_single_sequence_splits_both_paths():
+    """One sequence through varlen_attn with several splits: one query row
+    (vector path at G 4, matrix cores at G 8) and two rows (matrix cores)."""
+    for hq, q_len in ((32, 1), (64, 1), (32, 2), (64, 2)):
+        inp = workloads.paged_inputs(seed=79 + hq + q_len, lengths=[1000], q_lens=[q_len], q_heads=hq,
+                                     kv_heads=8, head_dim=128, dtype=torch.bfloat16, num_blocks=70,
+                                     max_blocks=64, causal=True, device=DEV)
+        ref = oracle_paged(inp)
+        for s in (0, 4, 16):
+            check_close(run_varlen_paged(inp, num_splits=s), ref, "bf16", f"hq={hq} q_len={q_len} splits={s}")
+
+
 def test_mixed_column_segments_small():
     """Ring store, causal + window, decode and chunked-prefill segments mixed;
     uncovered rows come back exactly 0."""
