@@ -94,7 +94,12 @@ __device__ __attribute__((aligned(16))) uint8_t kZeroRow[512];
 // and draft-verify workloads: with two row tiles a D = 128 wave fits two to a
 // SIMD and two 68 KiB work groups share a CU; at D = 256 two row tiles do not
 // fit two waves to a SIMD, and eight one-tile waves with four stages win.
-template <int D>
+// FEW: calls whose units have at most 64 rows (max_seqlen_q * group: decode
+// with a GQA group of 8) at D = 256.  There every row sits in the first wave
+// and the chunk stream binds, so four one-tile waves with two stages make a
+// 68 KiB work group, two share a CU, and a call of 16 splits of 4 sequences
+// and 8 kv heads fits one dispatch round (long-context decode 339 -> 276 us).
+template <int D, bool FEW = false>
 struct MfmaShape;
 template <>
 struct MfmaShape<64> { static constexpr int NW = 4, RT = 2, BN = 64, NS = 4, WPE = 2; };
@@ -102,6 +107,9 @@ template <>
 struct MfmaShape<128> { static constexpr int NW = 4, RT = 2, BN = 64, NS = 2, WPE = 2; };
 template <>
 struct MfmaShape<256> { static constexpr int NW = 8, RT = 1, BN = 32, NS = 4, WPE = 1; };
+template <>
+struct MfmaShape<256, true> { static constexpr int NW = 4, RT = 1, BN = 32, NS = 2, WPE = 2; };
+static_assert(MfmaShape<256, true>::BN == MfmaShape<256>::BN, "one chunk size per head_dim");
 
 template <int D, int NW, int RT, int BN, int NS>
 struct MfmaCfg {
@@ -712,16 +720,23 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     }
 }
 
-template <int D>
-constexpr int32_t shape_rows() { return 16 * MfmaShape<D>::NW * MfmaShape<D>::RT; }
+template <int D, bool FEW = false>
+constexpr int32_t shape_rows() { return 16 * MfmaShape<D, FEW>::NW * MfmaShape<D, FEW>::RT; }
 
-int32_t mfma_rows_per_group(int32_t head_dim) {
+// Whether a call whose units have up to `rows` rows (max_seqlen_q * group)
+// takes the few-rows shape.
+static bool few_rows(int32_t head_dim, int64_t rows) { return head_dim == 256 && rows <= shape_rows<256, true>(); }
+
+int32_t mfma_rows_per_group(int32_t head_dim, int64_t rows) {
+    if (few_rows(head_dim, rows)) return shape_rows<256, true>();
     return head_dim == 64 ? shape_rows<64>() : head_dim == 128 ? shape_rows<128>() : shape_rows<256>();
 }
 // Work groups of the matrix-core kernel one CU holds at once (LDS and
-// register budgets of the shape: 68 KiB / 2 waves per SIMD at D <= 128,
-// 132 KiB at D = 256).
-int32_t mfma_groups_per_cu(int32_t head_dim) { return head_dim == 256 ? 1 : 2; }
+// register budgets of the shape: 68 KiB / 2 waves per SIMD at D <= 128 and
+// for the few-rows shape, 132 KiB at D = 256).
+int32_t mfma_groups_per_cu(int32_t head_dim, int64_t rows) {
+    return head_dim == 256 && !few_rows(head_dim, rows) ? 1 : 2;
+}
 
 int32_t mfma_chunk_keys(int32_t head_dim) {
     return head_dim == 64 ? MfmaShape<64>::BN : head_dim == 128 ? MfmaShape<128>::BN : MfmaShape<256>::BN;
@@ -731,9 +746,9 @@ bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim) {
     return dtype == PKV_BF16 && (head_dim == 64 || head_dim == 128 || head_dim == 256);
 }
 
-template <int D, bool STREAM>
+template <int D, bool FEW, bool STREAM>
 static void launch_mfma_policy(const AttnParams& p, dim3 grid, hipStream_t stream) {
-    using Sh = MfmaShape<D>;
+    using Sh = MfmaShape<D, FEW>;
     if (p.mode == kColumn) {
         attn_mfma_kernel<D, Sh::NW, Sh::RT, Sh::BN, Sh::NS, Sh::WPE, false, STREAM><<<grid, dim3(64 * Sh::NW), 0, stream>>>(p);
     } else {
@@ -750,8 +765,15 @@ static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
     // with a group of 8: 364 -> 338 us; draft verify 470 -> 460 us).  With
     // several row tiles, the tiles of a unit read the same keys and the cached
     // policy keeps them (the column-store step ran 3 % slower streamed).
-    if (p.mfma_tiles == 1) launch_mfma_policy<D, true>(p, grid, stream);
-    else launch_mfma_policy<D, false>(p, grid, stream);
+    if constexpr (D == 256) {
+        if (few_rows(D, (int64_t)p.max_seqlen_q * p.group)) {
+            if (p.mfma_tiles != 1) return hipErrorInvalidValue;     // one tile holds every row
+            launch_mfma_policy<D, true, true>(p, grid, stream);
+            return hipGetLastError();
+        }
+    }
+    if (p.mfma_tiles == 1) launch_mfma_policy<D, false, true>(p, grid, stream);
+    else launch_mfma_policy<D, false, false>(p, grid, stream);
     return hipGetLastError();
 }
 

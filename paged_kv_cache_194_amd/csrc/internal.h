@@ -228,9 +228,12 @@ bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group);
 hipError_t launch_attn_mfma(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
                             hipStream_t stream);
 bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim);
-int32_t mfma_rows_per_group(int32_t head_dim);
+// Shape figures of the matrix-core launch for a call whose units have up to
+// `rows` = max_seqlen_q * group rows: rows per work group, keys per chunk,
+// work groups per CU.
+int32_t mfma_rows_per_group(int32_t head_dim, int64_t rows);
 int32_t mfma_chunk_keys(int32_t head_dim);
-int32_t mfma_groups_per_cu(int32_t head_dim);
+int32_t mfma_groups_per_cu(int32_t head_dim, int64_t rows);
 
 // Zero every output row of [0, total_q) that no unit covers.
 hipError_t launch_zero_uncovered(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,

@@ -217,8 +217,11 @@ def test_split_choice_rules():
     assert pkv.attn_num_splits(64, 1, 8192, 32, 8, 128, 0) == 4           # at least 4
     assert pkv.attn_num_splits(4, 1, 65536, 32, 8, 128, 0) == max(4, (2 * cus + 16) // 32)
     assert pkv.attn_num_splits(2, 1, 16384, 32, 8, 128, 0) == max(4, (2 * cus + 8) // 16)
-    # group 8 on the matrix cores: 4 units x 8 kv heads x 1 row tile = 32 items
-    assert pkv.attn_num_splits(4, 1, 65536, 64, 8, 256, 0) == (cus + 16) // 32
+    # group 8 on the matrix cores: 4 units x 8 kv heads x 1 row tile = 32 items; at
+    # head_dim 256 eight rows per unit take the four-wave shape, two work groups per CU
+    assert pkv.attn_num_splits(4, 1, 65536, 64, 8, 256, 0) == (2 * cus + 16) // 32
+    assert pkv.attn_num_splits(4, 8, 65536, 64, 8, 256, 0) == (2 * cus + 16) // 32    # 64 rows
+    assert pkv.attn_num_splits(4, 9, 65536, 64, 8, 256, 0) == (cus + 16) // 32        # 72 rows
     # matrix cores: 4 units x 8 kv heads x 1 row tile (16 rows x 8 heads = 128) = 32 items
     assert pkv.attn_num_splits(4, 16, 65536, 64, 8, 256, 0) == (cus + 16) // 32
     # 32 units x 8 kv heads x 16 row tiles (512 rows x 4 heads / 128) = 4096 items: one split
