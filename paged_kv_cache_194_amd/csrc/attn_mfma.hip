@@ -95,10 +95,12 @@ __device__ __attribute__((aligned(16))) uint8_t kZeroRow[512];
 // SIMD and two 68 KiB work groups share a CU; at D = 256 two row tiles do not
 // fit two waves to a SIMD, and eight one-tile waves with four stages win.
 // FEW: calls whose units have at most 64 rows (max_seqlen_q * group: decode
-// with a GQA group of 8) at D = 256.  There every row sits in the first wave
-// and the chunk stream binds, so four one-tile waves with two stages make a
-// 68 KiB work group, two share a CU, and a call of 16 splits of 4 sequences
-// and 8 kv heads fits one dispatch round (long-context decode 339 -> 276 us).
+// with a GQA group of 8 or 16) at D = 128 and 256.  There every row sits in
+// the first wave and the chunk stream binds, so four one-tile waves with two
+// stages make a 68 KiB work group and two share a CU: at D = 256 a call of 16
+// splits of 4 sequences and 8 kv heads then fits one dispatch round (4 x
+// 32K/64K keys, G 8: 339 -> 276 us); at D = 128 the first wave computes one
+// row tile instead of two, empty, ones (same call: 178 -> 155 us).
 template <int D, bool FEW = false>
 struct MfmaShape;
 template <>
@@ -106,10 +108,16 @@ struct MfmaShape<64> { static constexpr int NW = 4, RT = 2, BN = 64, NS = 4, WPE
 template <>
 struct MfmaShape<128> { static constexpr int NW = 4, RT = 2, BN = 64, NS = 2, WPE = 2; };
 template <>
+struct MfmaShape<128, true> { static constexpr int NW = 4, RT = 1, BN = 64, NS = 2, WPE = 2; };
+template <>
 struct MfmaShape<256> { static constexpr int NW = 8, RT = 1, BN = 32, NS = 4, WPE = 1; };
 template <>
 struct MfmaShape<256, true> { static constexpr int NW = 4, RT = 1, BN = 32, NS = 2, WPE = 2; };
-static_assert(MfmaShape<256, true>::BN == MfmaShape<256>::BN, "one chunk size per head_dim");
+static_assert(MfmaShape<128, true>::BN == MfmaShape<128>::BN && MfmaShape<256, true>::BN == MfmaShape<256>::BN,
+              "one chunk size per head_dim");
+static_assert(16 * MfmaShape<128, true>::NW * MfmaShape<128, true>::RT ==
+                  16 * MfmaShape<256, true>::NW * MfmaShape<256, true>::RT,
+              "one row bound for the few-rows shapes");
 
 template <int D, int NW, int RT, int BN, int NS>
 struct MfmaCfg {
@@ -725,10 +733,12 @@ constexpr int32_t shape_rows() { return 16 * MfmaShape<D, FEW>::NW * MfmaShape<D
 
 // Whether a call whose units have up to `rows` rows (max_seqlen_q * group)
 // takes the few-rows shape.
-static bool few_rows(int32_t head_dim, int64_t rows) { return head_dim == 256 && rows <= shape_rows<256, true>(); }
+static bool few_rows(int32_t head_dim, int64_t rows) {
+    return (head_dim == 128 || head_dim == 256) && rows <= shape_rows<256, true>();
+}
 
 int32_t mfma_rows_per_group(int32_t head_dim, int64_t rows) {
-    if (few_rows(head_dim, rows)) return shape_rows<256, true>();
+    if (few_rows(head_dim, rows)) return head_dim == 128 ? shape_rows<128, true>() : shape_rows<256, true>();
     return head_dim == 64 ? shape_rows<64>() : head_dim == 128 ? shape_rows<128>() : shape_rows<256>();
 }
 // Work groups of the matrix-core kernel one CU holds at once (LDS and
@@ -765,7 +775,7 @@ static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
     // with a group of 8: 364 -> 338 us; draft verify 470 -> 460 us).  With
     // several row tiles, the tiles of a unit read the same keys and the cached
     // policy keeps them (the column-store step ran 3 % slower streamed).
-    if constexpr (D == 256) {
+    if constexpr (D == 128 || D == 256) {
         if (few_rows(D, (int64_t)p.max_seqlen_q * p.group)) {
             if (p.mfma_tiles != 1) return hipErrorInvalidValue;     // one tile holds every row
             launch_mfma_policy<D, true, true>(p, grid, stream);

@@ -131,22 +131,24 @@ def test_large_group_decode_through_mfma():
         check_close(out, ref, "bf16", f"G=16 splits={s}")
 
 
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("causal", [True, False])
-def test_few_rows_d256_shape(causal):
-    """Head_dim 256 calls whose units have at most 64 rows (max_seqlen_q * G)
-    take the four-wave shape: units of 1..8 rows at G 8 (rows in every wave of
-    the work group) and G 16 decode units, with and without splits."""
+def test_few_rows_shapes(causal, D):
+    """Head_dim 128 and 256 calls whose units have at most 64 rows
+    (max_seqlen_q * G) take the four-wave one-tile shape: units of 1..8 rows at
+    G 8 (rows in every wave of the work group) and G 16 decode units, with and
+    without splits."""
     lengths = [700, 9, 1500, 64, 333]
     q_lens = [8, 3, 1, 5, 8]
-    inp = workloads.paged_inputs(seed=780 + causal, lengths=lengths, q_lens=q_lens, q_heads=64, kv_heads=8,
-                                 head_dim=256, dtype=torch.bfloat16, num_blocks=200, max_blocks=100,
+    inp = workloads.paged_inputs(seed=780 + causal + D, lengths=lengths, q_lens=q_lens, q_heads=64, kv_heads=8,
+                                 head_dim=D, dtype=torch.bfloat16, num_blocks=200, max_blocks=100,
                                  causal=causal, device=DEV)
     assert inp.max_seqlen_q * 8 <= 64
     ref = oracle_paged(inp)
     for s in (0, 1, 3):
         check_close(run_varlen_paged(inp, num_splits=s), ref, "bf16", f"G8 causal={causal} splits={s}")
-    dec = workloads.paged_inputs(seed=790 + causal, lengths=[1, 500, 2100], q_lens=[1] * 3, q_heads=64,
-                                 kv_heads=4, head_dim=256, dtype=torch.bfloat16, num_blocks=200,
+    dec = workloads.paged_inputs(seed=790 + causal + D, lengths=[1, 500, 2100], q_lens=[1] * 3, q_heads=64,
+                                 kv_heads=4, head_dim=D, dtype=torch.bfloat16, num_blocks=200,
                                  max_blocks=140, causal=causal, device=DEV)
     ref = oracle_paged(dec)
     for s in (0, 1, 5):
