@@ -192,19 +192,37 @@ __device__ __forceinline__ void deal_for_each(const DealItems& d, const F& item_
         if (d.ib + k < d.ie) body(d.ib + k, d.n[k]);
     for (int32_t i = d.ib + kDealRegs; i < d.ie; ++i) body(i, item_n(i));
 }
+// Sum (MAX: maximum) of x over the wave's 64 lanes, wave-uniform: four DPP
+// steps within rows of 16 lanes, one swizzle across the two rows of each
+// half, and the halves read out of lanes 0 and 32.  No step goes through a
+// cross-lane LDS permute (ds_bpermute), whose round trip a chain of six per
+// reduction had paid.
+template <bool MAX>
+__device__ __forceinline__ int32_t wave_reduce_i32(int32_t x) {
+    auto op = [](int32_t a, int32_t b) { return MAX ? max(a, b) : a + b; };
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, kQuadXor1, 0xF, 0xF, false));
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, kQuadXor2, 0xF, 0xF, false));
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, kRowHalfMirror, 0xF, 0xF, false));
+    x = op(x, __builtin_amdgcn_update_dpp(0, x, kRowMirror, 0xF, 0xF, false));
+    x = op(x, __builtin_amdgcn_ds_swizzle(x, 0x401F));
+    return op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 32));
+}
+
 template <typename F>
 __device__ int32_t deal_size(const DealItems& d, const F& item_n, int64_t slots) {
     int32_t nmax = 0;
     deal_for_each(d, item_n, [&](int32_t, int32_t n) { nmax = max(nmax, n); });
-#pragma unroll
-    for (int st = 1; st < 64; st *= 2) nmax = max(nmax, __shfl_xor(nmax, st, 64));
+    nmax = wave_reduce_i32<true>(nmax);
     int32_t lo = 1, hi = nmax > 1 ? nmax : 1;      // c = nmax gives one slot per item
+    // Only whether the count fits `slots` matters (at most the grid's 65535
+    // rows): each lane's count saturates at cap, so the wave's sum stays far
+    // inside 32 bits whatever the items' sizes.
+    const int32_t cap = slots < (1 << 24) ? (int32_t)slots + 1 : (1 << 24);
     while (lo < hi) {                              // wave-uniform loop
         const int32_t c = lo + (hi - lo) / 2;
-        int64_t k = 0;
-        deal_for_each(d, item_n, [&](int32_t, int32_t n) { k += deal_slots_of(n, c); });
-#pragma unroll
-        for (int st = 1; st < 64; st *= 2) k += __shfl_xor(k, st, 64);
+        int32_t k = 0;
+        deal_for_each(d, item_n, [&](int32_t, int32_t n) { k = min(k + deal_slots_of(n, c), cap); });
+        k = wave_reduce_i32<false>(k);
         if (k <= slots) hi = c; else lo = c + 1;
     }
     return lo;
