@@ -1,6 +1,6 @@
 // Matrix-core (MFMA) attention for units with several query rows: chunked
-// prefill segments and draft-verify blocks, and any unit whose GQA group is
-// larger than the vector path holds.
+// prefill segments and draft-verify blocks, and the single-row units of bf16
+// calls whose GQA group is 8 or more.
 //
 // What it computes (ExecuTorch PR #24073, sdpa_varlen: causal and non-causal
 // query blocks over a column store or, with the same arithmetic, a paged cache;
@@ -11,19 +11,21 @@
 //
 // GQA packing: the unit's L positions times the G heads of one kv head form
 // M = L*G rows (row m: position m / G, head m % G), so every K/V element staged
-// for a kv head is used by all of its query heads.  A work group (NW waves)
-// takes BM = 16*NW of those rows and a range of 64-key chunks.
+// for a kv head is used by all of its query heads.  A work group (NW waves of
+// RT row tiles of 16) takes BM = 16*NW*RT of those rows and a range of
+// BN-key chunks (the launch shapes below).
 //
 // Per chunk the work group stages K and V row-major in LDS -- keys outside
 // the rows' union of visible ranges, or without storage, are staged as zeros --
-// and each wave runs two bf16 MFMA passes for its 16 rows with
+// and each wave runs two bf16 MFMA passes for each of its 16-row tiles with
 // v_mfma_f32_16x16x32_bf16:
 //   S^T[key][row] = K . Q^T     (A = K from LDS, B = Q^T from registers)
 //   O^T[d][row]  += V^T . P^T   (A = V^T built by transposing LDS reads,
 //                                ds_read_b64_tr_b16; B = P^T straight from the
 //                                C layout of S^T)
-// Chunks come from global memory through a ring of register slots, several
-// chunks ahead of the one being computed, into two LDS buffers.
+// Chunks go from global memory straight into a ring of NS LDS stages
+// (direct-to-LDS loads), NS - 1 chunks (NS - 2 with two wave groups one phase
+// apart) ahead of the one being computed.
 // Working transposed puts one query row per lane column, so the online-softmax
 // statistics and the rescale of O stay inside the lane (plus a 4-lane-group
 // max/sum).  The k order of the second product is the key permutation the

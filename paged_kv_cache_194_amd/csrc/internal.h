@@ -218,13 +218,15 @@ hipError_t launch_prefix_copy(bool to_dense, void* dst_k, void* dst_v, const voi
                               int32_t heads, int64_t row_bytes, int32_t* seqused_k,
                               hipStream_t stream);
 
-// Vector-ALU path for units with one query row (q_len == 1) and group <= 8.
-// Returns hipErrorInvalidValue when no kernel is compiled for (dtype, D, group).
+// Vector-ALU path for units with one query row (q_len == 1) and group <= 8
+// (the library routes bf16 groups of 8 to the matrix cores; the kernel takes
+// them too).  Returns hipErrorInvalidValue when no kernel is compiled for (dtype, D, group).
 hipError_t launch_attn_vec(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
                            hipStream_t stream);
 bool attn_vec_supported(pkv_dtype dtype, int32_t head_dim, int32_t group);
 
-// Matrix-core path for units with several query rows (or a group > 8): bf16.
+// Matrix-core path for units with several query rows, and single-row units
+// with a group of 8 or more: bf16.
 hipError_t launch_attn_mfma(const AttnParams& p, pkv_dtype dtype, int32_t head_dim,
                             hipStream_t stream);
 bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim);
