@@ -439,6 +439,22 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
         }
     };
 
+    // LDS byte offsets of this lane's reads inside a stage, for key tile 0 and
+    // PV step 0: the swizzle of a row depends on the row modulo 16 (column XOR)
+    // or 8 (rotation) only, so later key tiles and PV steps add whole 16-row
+    // blocks, an immediate offset of the read.
+    int32_t k_off[KS], v_off[DT];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_off[ks] = lr * RB + C::swz(lr, ks * 4 + lq) * 16;
+    {
+        const int vr0b = 4 * lq + (lr >> 2);
+        const int half = (lr & 1) * 8;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) v_off[dt] = vr0b * RB + C::swz(vr0b, 2 * dt + ((lr & 3) >> 1)) * 16 + half;
+    }
+    // (Recomputed at every read, these offsets cost the head_dim-256 draft pass
+    // 2 %, and 12-22 more VGPRs.)
+
     // A wave issues its two MFMA passes at raised priority and its softmax at
     // the normal one, so that on a SIMD shared with a wave of another phase
     // the matrix core is fed first and the VALU work fills the gaps (the
@@ -454,8 +470,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             for (int rt = 0; rt < RT; ++rt) st[rt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int row = kt * 16 + lr;
-                const u32x4 a = *reinterpret_cast<const u32x4*>(sKb + row * RB + C::swz(row, ks * 4 + lq) * 16);
+                const u32x4 a = *reinterpret_cast<const u32x4*>(sKb + kt * 16 * RB + k_off[ks]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) st[rt][kt] = mfma16(a, qf[rt][ks], st[rt][kt]);
             }
@@ -542,17 +557,14 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
                 b[rt] = u32x4{pk[rt][2 * s2][0], pk[rt][2 * s2][1], pk[rt][2 * s2 + 1][0], pk[rt][2 * s2 + 1][1]};
-            const int kk0 = s2 * 32 + 4 * lq;
-            // A = V^T rows d = dt*16 + lr, keys {kk0..kk0+3, kk0+16..kk0+19}: two
-            // transposing reads of row-major V; lane (4m + c) of a 16-lane group
-            // names row kk0 + m, elements dt*16 + 4c .. +3 (8 bytes of a 16-byte column).
-            const int vr0 = kk0 + (lr >> 2), vr1 = vr0 + 16;
-            const int half = (lr & 1) * 8;
+            // A = V^T rows d = dt*16 + lr, keys {kk0..kk0+3, kk0+16..kk0+19},
+            // kk0 = s2*32 + 4*lq: two transposing reads of row-major V; lane
+            // (4m + c) of a 16-lane group names row kk0 + m, elements
+            // dt*16 + 4c .. +3 (8 bytes of a 16-byte column).
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int cl = 2 * dt + ((lr & 3) >> 1);
-                const v4i16 lo4 = ds_read_tr16(sVb + vr0 * RB + C::swz(vr0, cl) * 16 + half);
-                const v4i16 hi4 = ds_read_tr16(sVb + vr1 * RB + C::swz(vr1, cl) * 16 + half);
+                const v4i16 lo4 = ds_read_tr16(sVb + s2 * 32 * RB + v_off[dt]);
+                const v4i16 hi4 = ds_read_tr16(sVb + (s2 * 32 + 16) * RB + v_off[dt]);
                 const u32x4 a = u32x4{pair_bits(lo4, 0), pair_bits(lo4, 1), pair_bits(hi4, 0), pair_bits(hi4, 1)};
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma16(a, b[rt], o[rt][dt]);
