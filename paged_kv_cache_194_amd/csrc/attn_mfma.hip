@@ -68,6 +68,23 @@ constexpr int kIdWindow = 1024;   // block ids staged in LDS at a time
 // Issued from inline assembly so that the compiler's wait-count bookkeeping
 // does not serialize it; the kernel places its own waits.  STREAM: nontemporal
 // (streaming) cache policy, for keys no other work group of the call reads.
+// The same load from the wave-uniform base `sbase` (an SGPR pair) plus this
+// lane's 32-bit byte offset `voff`.
+template <bool STREAM>
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
+    if constexpr (STREAM) {
+        asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+    } else {
+        asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+    }
+}
+// A 64-bit value known to be wave-uniform, moved to scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
 template <bool STREAM>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
     if constexpr (STREAM) {
@@ -368,9 +385,32 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     // are set when its chunk is issued and read when it is computed.
     static_assert(KT * NS <= 32, "storage mask bits");
     uint32_t nostore = 0u;
+    // Load m of this lane in a chunk that takes the uniform-base path: the
+    // byte offset from the chunk's base, fixed for the whole loop.  Every
+    // wave load covers rows of one 16-key tile (64 / RC rows, RC a power of
+    // two dividing 64).
+    static_assert(64 % RC == 0 && 16 % (64 / RC) == 0, "a wave load stays inside one 16-key tile");
+    const int64_t row_stride = (int64_t)p.cols * tok_stride;        // ring: bytes per store row
+    uint32_t issue_off[IPW];
+#pragma unroll
+    for (int m = 0; m < IPW; ++m) {
+        const int place = (wave + NW * m) * 64 + lane;
+        const int r = place / RC, cs = place - (place / RC) * RC;
+        const int64_t o = PAGED ? (int64_t)(r & 15) * tok_stride + head_off + C::unswz(r, cs) * 16
+                                : (int64_t)r * row_stride + head_off + C::unswz(r, cs) * 16;
+        issue_off[m] = (uint32_t)o;
+    }
+    // The lane offsets must fit the 32-bit offset of the uniform-base path.
+    const bool col_fast = (PAGED ? (int64_t)15 * tok_stride : (int64_t)(BN - 1) * row_stride) + head_off + RB <
+                          ((int64_t)1 << 31);
     auto issue = [&](int32_t c, int st) __attribute__((always_inline)) {
         const int32_t c0 = c_base + c * BN;
         const bool chunk_ok = c < c_end;
+        // A chunk inside every row's range whose keys all have storage (and,
+        // in a ring, do not wrap) is issued from one wave-uniform base per
+        // load plus the lane's fixed offset, with no per-lane address work.
+        bool fast = chunk_ok && c0 >= key_lo && c0 + BN <= key_hi;
+        int32_t tid_k[KT];
         if constexpr (PAGED) {
             uint32_t bad = 0u;
             if (chunk_ok) {
@@ -379,15 +419,38 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
                     int32_t w = (c0 >> 4) + k - id_base;
                     w = w < 0 ? 0 : (w >= kIdWindow ? kIdWindow - 1 : w);
                     const int32_t id = sIds[w];
+                    tid_k[k] = id;
                     bad |= (id >= 0 && id < p.num_blocks) ? 0u : (1u << k);
                 }
             }
             const uint32_t field = ((1u << KT) - 1u) << (KT * st);
             nostore = (nostore & ~field) | (bad << (KT * st));
+            fast = fast && bad == 0u && col_fast;
         }
         const uint32_t kdst = lds_addr(&sKV[st][0]), vdst = lds_addr(&sKV[st][CB]);
         int32_t ring0 = 0;
-        if constexpr (!PAGED) ring0 = c0 % p.rows;
+        if constexpr (!PAGED) {
+            ring0 = c0 % p.rows;
+            fast = fast && col_fast && ring0 + BN <= p.rows;
+        }
+        if (fast) {
+#pragma unroll
+            for (int m = 0; m < IPW; ++m) {
+                const int I = wave + NW * m;
+                int64_t a;
+                if constexpr (PAGED) {
+                    const int tile = (I * (64 / RC)) >> 4;          // the 16-key tile of load m
+                    a = (int64_t)__builtin_amdgcn_readfirstlane(tid_k[tile]) * blk_stride;
+                } else {
+                    a = (int64_t)ring0 * row_stride + (int64_t)ui.col * tok_stride;
+                }
+                const uint8_t* kb = uniform_ptr(Kg + a);
+                const uint8_t* vb = uniform_ptr(Vg + a);
+                dma16s<STREAM>(issue_off[m], kb, (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024)));
+                dma16s<STREAM>(issue_off[m], vb, (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024)));
+            }
+            return;
+        }
         const uint8_t* ks[IPW];
         const uint8_t* vs[IPW];
 #pragma unroll
