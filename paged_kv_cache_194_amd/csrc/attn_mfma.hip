@@ -578,8 +578,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) cmax = fmaxf(cmax, st[rt][kt][e]);
             }
-            cmax = fmaxf(cmax, xor_lanes<16>(cmax));
-            cmax = fmaxf(cmax, xor_lanes<32>(cmax));
+            cmax = swap_op16<true>(cmax);
+            cmax = swap_op32<true>(cmax);
             const float cm = cmax == -INFINITY ? -INFINITY : cmax * sc;   // scaled, log2 units
             const float m_new = fmaxf(m_run[rt], cm);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -711,8 +711,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     // Row sums across the 4 lane groups.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        l_run[rt] += xor_lanes<16>(l_run[rt]);
-        l_run[rt] += xor_lanes<32>(l_run[rt]);
+        l_run[rt] = swap_op16<false>(l_run[rt]);
+        l_run[rt] = swap_op32<false>(l_run[rt]);
     }
 
     // This lane holds O^T[d][row] for d = dt*16 + 4*lq + e of each of its rows.

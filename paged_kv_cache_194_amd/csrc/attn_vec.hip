@@ -592,8 +592,8 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
                 else if (st == 2) x += xor_lanes<2>(x);
                 else if (st == 4) x += xor_lanes<4>(x);
                 else if (st == 8) x += xor_lanes<8>(x);
-                else if (st == 16) x += xor_lanes<16>(x);
-                else x += xor_lanes<32>(x);
+                else if (st == 16) x = swap_op16<false>(x);
+                else x = swap_op32<false>(x);
             }
         }
         return x;

@@ -89,11 +89,33 @@ constexpr int kRowMirror = 0x140;     // lane i <- 15-i within 16
 constexpr int kRowRor4 = 0x124;       // lane i <- (i+4)%16 within a row
 constexpr int kRowRor8 = 0x128;       // lane i <- (i+8)%16 within a row
 
-__device__ __forceinline__ float swz_xor16(float x) {
-    // ds_swizzle bitmask mode: and 0x1F, or 0, xor 0x10 (within 32-lane halves)
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
-}
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// A copy of v the compiler cannot see through: the lane-swap builtins below
+// are folded wrongly when both of their operands are the same value (the
+// second result is taken to equal the first).
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+// op(x, x of lane ^ 32) and op(x, x of lane ^ 16) (op: max or sum) through
+// gfx950's v_permlane32_swap / v_permlane16_swap, VALU instructions with no
+// LDS round trip.  With x in both operands the two results hold, in every
+// lane, x of the lower and of the upper lane of its pair.
+template <bool MAX>
+__device__ __forceinline__ float swap_op32(float x) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(b, opaque_copy(b), false, false);
+    const float lo = __builtin_bit_cast(float, (uint32_t)r[0]), hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+    return MAX ? fmaxf(lo, hi) : lo + hi;
+}
+template <bool MAX>
+__device__ __forceinline__ float swap_op16(float x) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(b, opaque_copy(b), false, false);
+    const float lo = __builtin_bit_cast(float, (uint32_t)r[0]), hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+    return MAX ? fmaxf(lo, hi) : lo + hi;
+}
 
 // x from lane (lane ^ ST), ST = 1 .. 32.
 template <int ST>
@@ -115,8 +137,8 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (N >= 4) x += dpp<kQuadXor2>(x);
     if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
     if constexpr (N >= 16) x += dpp<kRowMirror>(x);
-    if constexpr (N >= 32) x += swz_xor16(x);
-    if constexpr (N >= 64) x += xor32(x);
+    if constexpr (N >= 32) x = swap_op16<false>(x);
+    if constexpr (N >= 64) x = swap_op32<false>(x);
     return x;
 }
 
@@ -127,8 +149,8 @@ __device__ __forceinline__ float across_groups(float x) {
     auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
     if constexpr (STRIDE <= 8) x = op(x, dpp<kRowRor8>(x));
     if constexpr (STRIDE <= 4) x = op(x, dpp<kRowRor4>(x));
-    if constexpr (STRIDE <= 16) x = op(x, swz_xor16(x));
-    if constexpr (STRIDE <= 32) x = op(x, xor32(x));
+    if constexpr (STRIDE <= 16) x = swap_op16<MAX>(x);
+    if constexpr (STRIDE <= 32) x = swap_op32<MAX>(x);
     return x;
 }
 
