@@ -587,20 +587,26 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             moved |= alpha[rt] != 1.f;
             m_run[rt] = m_new;
             float psum = 0.f;
+            // keep(kt, e): key kt*4 + e of the lane enters the sums.  Unmasked
+            // chunks (wave-uniform) take an instantiation with no per-key test.
+            auto probs = [&](auto keep) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                float pr[4];
+                for (int kt = 0; kt < KT; ++kt) {
+                    float pr[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = fmaf(st[rt][kt][e], sc, -m_use);
-                    pr[e] = fast_exp2(((vis >> (kt * 4 + e)) & 1u) ? x : -INFINITY);
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = fmaf(st[rt][kt][e], sc, -m_use);
+                        pr[e] = fast_exp2(keep(kt, e) ? x : -INFINITY);
+                    }
+                    // rounded to bf16 for the MFMA; the row sum adds the same rounded values
+                    pk[rt][kt][0] = pack_bf16(pr[0], pr[1]);
+                    pk[rt][kt][1] = pack_bf16(pr[2], pr[3]);
+                    psum = dot2_bf16(pk[rt][kt][0], kBf16OnePair, psum);
+                    psum = dot2_bf16(pk[rt][kt][1], kBf16OnePair, psum);
                 }
-                // rounded to bf16 for the MFMA; the row sum adds the same rounded values
-                pk[rt][kt][0] = pack_bf16(pr[0], pr[1]);
-                pk[rt][kt][1] = pack_bf16(pr[2], pr[3]);
-                psum = dot2_bf16(pk[rt][kt][0], kBf16OnePair, psum);
-                psum = dot2_bf16(pk[rt][kt][1], kBf16OnePair, psum);
-            }
+            };
+            if (masked) probs([&](int kt, int e) { return ((vis >> (kt * 4 + e)) & 1u) != 0u; });
+            else probs([](int, int) { return true; });
             l_run[rt] = l_run[rt] * alpha[rt] + psum;
         }
         if (__ballot(moved) != 0) {               // some row's max moved
