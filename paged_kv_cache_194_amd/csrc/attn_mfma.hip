@@ -61,6 +61,8 @@ __device__ __forceinline__ uint32_t pair_bits(const v4i16& v, int h) {
 }
 
 constexpr int kIdWindow = 1024;   // block ids staged in LDS at a time
+// Slack of the softmax reference point, in log2 units (probabilities < 256).
+constexpr float kLazyLog2 = 8.f;
 
 
 // Direct-to-LDS 16-byte load (global_load_lds_dwordx4): lane i's 16 bytes from
@@ -581,10 +583,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             cmax = swap_op16<true>(cmax);
             cmax = swap_op32<true>(cmax);
             const float cm = cmax == -INFINITY ? -INFINITY : cmax * sc;   // scaled, log2 units
-            const float m_new = fmaxf(m_run[rt], cm);
+            // The row's reference point moves only when a chunk's maximum
+            // passes it by more than kLazyLog2: probabilities stay below
+            // 2^kLazyLog2 (exact in the fp32 sums, the same relative rounding
+            // in bf16), and most chunks skip the rescale of O.
+            const bool bump = cm > m_run[rt] + kLazyLog2;
+            const float m_new = bump ? cm : m_run[rt];
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            alpha[rt] = fast_exp2(m_run[rt] - m_use);
-            moved |= alpha[rt] != 1.f;
+            alpha[rt] = bump ? fast_exp2(m_run[rt] - m_use) : 1.f;
+            moved |= bump;
             m_run[rt] = m_new;
             float psum = 0.f;
             // keep(kt, e): key kt*4 + e of the lane enters the sums.  Unmasked
