@@ -149,8 +149,8 @@ Plan make_plan(int32_t units, int32_t max_seqlen_q, int32_t keys, int32_t q_head
         pl.bm = pkv::mfma_rows_per_group(head_dim, rows);
         pl.tiles = (int32_t)((rows + pl.bm - 1) / pl.bm);
         const int64_t base = (int64_t)U * kv_heads * pl.tiles;
-        const int64_t chunks = ((int64_t)(keys > 0 ? keys : 1) + pkv::mfma_chunk_keys(head_dim) - 1) /
-                               pkv::mfma_chunk_keys(head_dim);
+        const int64_t chunks = ((int64_t)(keys > 0 ? keys : 1) + pkv::mfma_chunk_keys(head_dim, rows) - 1) /
+                               pkv::mfma_chunk_keys(head_dim, rows);
         // Library choice: about one round of work groups on the device (the
         // dealt splits are equal in size, and every split adds a BM x D partial
         // to merge), at least 8 chunks per split.

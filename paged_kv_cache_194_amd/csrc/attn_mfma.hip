@@ -24,8 +24,7 @@
 //                                ds_read_b64_tr_b16; B = P^T straight from the
 //                                C layout of S^T)
 // Chunks go from global memory straight into a ring of NS LDS stages
-// (direct-to-LDS loads), NS - 1 chunks (NS - 2 with two wave groups one phase
-// apart) ahead of the one being computed.
+// (direct-to-LDS loads), NS - 1 chunks ahead of the one being computed.
 // Working transposed puts one query row per lane column, so the online-softmax
 // statistics and the rescale of O stay inside the lane (plus a 4-lane-group
 // max/sum).  The k order of the second product is the key permutation the
@@ -114,7 +113,9 @@ __device__ __attribute__((aligned(16))) uint8_t kZeroRow[512];
 // least WPE waves per SIMD (a register cap).  Measured on the chunked-prefill
 // and draft-verify workloads: with two row tiles a D = 128 wave fits two to a
 // SIMD and two 68 KiB work groups share a CU; at D = 256 two row tiles do not
-// fit two waves to a SIMD, and eight one-tile waves with four stages win.
+// fit two waves to a SIMD, and eight one-tile waves win, with two stages of
+// 64-key chunks (draft verify 428 -> 407 us against four stages of 32 keys,
+// once the per-chunk instruction count had been cut).
 // FEW: calls whose units have at most 64 rows (max_seqlen_q * group: decode
 // with a GQA group of 8 or 16) at D = 128 and 256.  There every row sits in
 // the first wave and the chunk stream binds, so four one-tile waves with two
@@ -131,11 +132,9 @@ struct MfmaShape<128> { static constexpr int NW = 4, RT = 2, BN = 64, NS = 2, WP
 template <>
 struct MfmaShape<128, true> { static constexpr int NW = 4, RT = 1, BN = 64, NS = 2, WPE = 2; };
 template <>
-struct MfmaShape<256> { static constexpr int NW = 8, RT = 1, BN = 32, NS = 4, WPE = 1; };
+struct MfmaShape<256> { static constexpr int NW = 8, RT = 1, BN = 64, NS = 2, WPE = 1; };
 template <>
 struct MfmaShape<256, true> { static constexpr int NW = 4, RT = 1, BN = 32, NS = 2, WPE = 2; };
-static_assert(MfmaShape<128, true>::BN == MfmaShape<128>::BN && MfmaShape<256, true>::BN == MfmaShape<256>::BN,
-              "one chunk size per head_dim");
 static_assert(16 * MfmaShape<128, true>::NW * MfmaShape<128, true>::RT ==
                   16 * MfmaShape<256, true>::NW * MfmaShape<256, true>::RT,
               "one row bound for the few-rows shapes");
@@ -225,8 +224,6 @@ template <int D, int NW, int RT, int BN, int NS, int WPE, bool PAGED, bool STREA
 __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     using C = MfmaCfg<D, NW, RT, BN, NS>;
     constexpr bool kMfmaPrio = D <= 128;
-    constexpr bool kRot = NW >= 8;                // two wave groups one phase apart (see the chunk loop)
-    static_assert(!kRot || NS >= 4, "the second wave group keeps a chunk's V one step longer");
     constexpr int NT = C::NT, BM = C::BM, RB = C::RB, RC = C::RC, CB = C::CB, IPW = C::IPW,
                   KT = C::KT, KS = C::KS, DT = C::DT;
 
@@ -656,50 +653,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     // Loads past the range read the zero row, so every step waits for the
     // same count.
     const int32_t n = c_end > c_first ? c_end - c_first : 0;
-    if constexpr (kRot) {
-      if (n > 0) {
-        // Eight waves, two to a SIMD: waves 0..3 run each chunk's scores,
-        // softmax and PV in the step the chunk lands; waves 4..7 (the other
-        // wave of every SIMD) run the softmax and PV of the chunk before, then
-        // the scores of this one, so that on each SIMD one wave's exponentials
-        // meet the other's products instead of the same phase.  A chunk's V is
-        // read one step later by the second group, so loads run NS - 2 chunks
-        // ahead: step i waits for chunk i, barrier, issues chunk i + NS - 2
-        // into the stage of chunk i - 2, computes.  Step n only finishes the
-        // second group's last chunk.
-        const bool late = wave >= NW / 2;
-#pragma unroll
-        for (int s = 0; s < NS - 2; ++s) {
-            if (s < n) ensure_ids(c_first + s);
-            issue(c_first + s, s);
-        }
-        f32x4_t sprev[RT][KT];                    // second group: scores of the chunk before
-        for (int32_t i = 0; i <= n; ++i) {
-            wait_vm<2 * IPW * (NS - 3)>();
-            __builtin_amdgcn_s_barrier();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (i + NS - 2 < n) ensure_ids(c_first + i + NS - 2);
-            issue(c_first + i + NS - 2, (i + NS - 2) % NS);
-            if (!wave_idle) {
-                const int st = i % NS;
-                if (!late) {
-                    if (i < n) {
-                        f32x4_t sc4[RT][KT];
-                        qk(&sKV[st][0], sc4);
-                        softmax_pv(c_first + i, st, sc4, &sKV[st][CB]);
-                    }
-                } else {
-                    if (i > 0) {
-                        const int sp = (i - 1) % NS;
-                        softmax_pv(c_first + i - 1, sp, sprev, &sKV[sp][CB]);
-                    }
-                    if (i < n) qk(&sKV[st][0], sprev);
-                }
-            }
-        }
-        wait_vm<0>();                             // no load may land after the work group ends
-      }
-    } else if (n > 0) {
+    if (n > 0) {
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s) {
             if (s < n) ensure_ids(c_first + s);
@@ -838,7 +792,8 @@ int32_t mfma_groups_per_cu(int32_t head_dim, int64_t rows) {
     return head_dim == 256 && !few_rows(head_dim, rows) ? 1 : 2;
 }
 
-int32_t mfma_chunk_keys(int32_t head_dim) {
+int32_t mfma_chunk_keys(int32_t head_dim, int64_t rows) {
+    if (few_rows(head_dim, rows)) return head_dim == 128 ? MfmaShape<128, true>::BN : MfmaShape<256, true>::BN;
     return head_dim == 64 ? MfmaShape<64>::BN : head_dim == 128 ? MfmaShape<128>::BN : MfmaShape<256>::BN;
 }
 

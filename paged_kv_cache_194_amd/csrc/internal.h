@@ -234,7 +234,7 @@ bool attn_mfma_supported(pkv_dtype dtype, int32_t head_dim);
 // `rows` = max_seqlen_q * group rows: rows per work group, keys per chunk,
 // work groups per CU.
 int32_t mfma_rows_per_group(int32_t head_dim, int64_t rows);
-int32_t mfma_chunk_keys(int32_t head_dim);
+int32_t mfma_chunk_keys(int32_t head_dim, int64_t rows);
 int32_t mfma_groups_per_cu(int32_t head_dim, int64_t rows);
 
 // Zero every output row of [0, total_q) that no unit covers.
