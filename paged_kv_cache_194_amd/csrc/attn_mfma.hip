@@ -400,7 +400,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
         issue_off[m] = (uint32_t)o;
     }
     // The lane offsets must fit the 32-bit offset of the uniform-base path.
-    const bool col_fast = (PAGED ? (int64_t)15 * tok_stride : (int64_t)(BN - 1) * row_stride) + head_off + RB <
+    const bool offs_fit = (PAGED ? (int64_t)15 * tok_stride : (int64_t)(BN - 1) * row_stride) + head_off + RB <
                           ((int64_t)1 << 31);
     auto issue = [&](int32_t c, int st) __attribute__((always_inline)) {
         const int32_t c0 = c_base + c * BN;
@@ -424,13 +424,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
             }
             const uint32_t field = ((1u << KT) - 1u) << (KT * st);
             nostore = (nostore & ~field) | (bad << (KT * st));
-            fast = fast && bad == 0u && col_fast;
+            fast = fast && bad == 0u && offs_fit;
         }
         const uint32_t kdst = lds_addr(&sKV[st][0]), vdst = lds_addr(&sKV[st][CB]);
         int32_t ring0 = 0;
         if constexpr (!PAGED) {
             ring0 = c0 % p.rows;
-            fast = fast && col_fast && ring0 + BN <= p.rows;
+            fast = fast && offs_fit && ring0 + BN <= p.rows;
         }
         if (fast) {
 #pragma unroll
