@@ -41,6 +41,8 @@
 namespace pkv {
 
 constexpr int kWaves = 4;
+// Slack of the softmax reference point, in log2 units (probabilities < 256).
+constexpr float kLazyLog2 = 8.f;
 constexpr int kThreads = 64 * kWaves;
 
 template <typename T, int D, int GT>
@@ -463,10 +465,14 @@ __global__ __launch_bounds__(kThreads, (vec_waves_per_simd<T, D, GT>())) void at
 #pragma unroll
             for (int j = 1; j < KNI; ++j) mb = fmaxf(mb, s[j][r]);
             mb = across_groups<KLPT, true>(mb);
-            const float m_new = fmaxf(m[r], mb);
+            // The head's reference point moves only when a block's maximum
+            // passes it by more than kLazyLog2 (probabilities stay below
+            // 2^kLazyLog2), so most blocks skip the rescale.
+            const bool bump = mb > m[r] + kLazyLog2;
+            const float m_new = bump ? mb : m[r];
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            alpha[r] = fast_exp2(m[r] - m_use);
-            rescale |= (m_new != m[r]);
+            alpha[r] = bump ? fast_exp2(m[r] - m_use) : 1.f;
+            rescale |= bump;
             m[r] = m_new;
 #pragma unroll
             for (int j = 0; j < KNI; ++j) {
