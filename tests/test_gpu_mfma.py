@@ -177,13 +177,15 @@ def test_single_sequence_splits_both_paths():
             check_close(run_varlen_paged(inp, num_splits=s), ref, "bf16", f"hq={hq} q_len={q_len} splits={s}")
 
 
-def test_mixed_column_segments_small():
-    """Ring store, causal + window, decode and chunked-prefill segments mixed;
-    uncovered rows come back exactly 0."""
+@pytest.mark.parametrize("D,hq", [(128, 32), (256, 64), (64, 32)])
+def test_mixed_column_segments_small(D, hq):
+    """Ring store, causal + window, decode and chunked-prefill segments mixed
+    (chunks that wrap the ring and chunks that do not); uncovered rows come
+    back exactly 0."""
     q_lens = [1, 1, 37, 1, 90, 16, 1]
     ends = [5, 700, 900, 1500, 3000, 40, 64]
-    inp = workloads.column_inputs(seed=75, rows=512, cols=8, q_lens=q_lens, kv_ends=ends, total_q=220,
-                                  q_heads=32, kv_heads=8, head_dim=128, dtype=torch.bfloat16, causal=True,
+    inp = workloads.column_inputs(seed=75 + D, rows=512, cols=8, q_lens=q_lens, kv_ends=ends, total_q=220,
+                                  q_heads=hq, kv_heads=8, head_dim=D, dtype=torch.bfloat16, causal=True,
                                   window=300, device=DEV)
     pkv.kv_append(inp.k_store, inp.v_store, inp.k_new, inp.v_new, ring_slots(inp))
     ref = oracle_column(inp)
@@ -195,7 +197,7 @@ def test_mixed_column_segments_small():
                         softmax_scale=inp.scale, causal=True, window=300, num_splits=s)
         torch.cuda.synchronize()
         assert (out[~covered] == 0).all()
-        check_close(out, ref, "bf16", f"column splits={s}")
+        check_close(out, ref, "bf16", f"column D={D} splits={s}")
 
 
 def _column_full_check(inp, out, q, what):
