@@ -269,12 +269,14 @@ def test_long_context_draft_and_decode_full_size():
         _paged_full_check(dec, out_d, qs, f"decode x{scale_q}")
 
 
-def test_block_without_storage_inside_live_range():
+@pytest.mark.parametrize("D", [128, 256])
+def test_block_without_storage_inside_live_range(D):
     """A block-table entry outside the pool inside a unit's live range: its 16
     keys contribute nothing to any row (multi-row causal units on the matrix
-    cores, and a GQA group of 16 in paged_decode_attn)."""
-    inp = workloads.paged_inputs(seed=76, lengths=[100, 260, 64], q_lens=[20, 33, 16], q_heads=32,
-                                 kv_heads=8, head_dim=128, dtype=torch.bfloat16, num_blocks=40,
+    cores, and a GQA group of 16 in paged_decode_attn).  The chunks around
+    such a block take the per-lane load path, the others the uniform-base one."""
+    inp = workloads.paged_inputs(seed=76 + D, lengths=[100, 260, 64], q_lens=[20, 33, 16], q_heads=32,
+                                 kv_heads=8, head_dim=D, dtype=torch.bfloat16, num_blocks=40,
                                  max_blocks=20, causal=True, device=DEV)
     inp.block_table[0, 2] = -1                   # keys 32..47 of unit 0
     inp.block_table[1, 15] = 1 << 30             # keys 240..255 of unit 1: seen by its last rows
@@ -282,8 +284,8 @@ def test_block_without_storage_inside_live_range():
     ref = oracle_paged(inp)
     for s in (0, 1, 3):
         check_close(run_varlen_paged(inp, num_splits=s), ref, "bf16", f"multi-row splits={s}")
-    dec = workloads.paged_inputs(seed=77, lengths=[1, 500, 64, 2000], q_lens=[1] * 4, q_heads=32, kv_heads=2,
-                                 head_dim=128, dtype=torch.bfloat16, num_blocks=200, max_blocks=128, device=DEV)
+    dec = workloads.paged_inputs(seed=77 + D, lengths=[1, 500, 64, 2000], q_lens=[1] * 4, q_heads=32, kv_heads=2,
+                                 head_dim=D, dtype=torch.bfloat16, num_blocks=200, max_blocks=128, device=DEV)
     dec.block_table[1, 3] = -7
     dec.block_table[3, 100] = 200
     dec.block_table[2, 3] = -1                   # the last live block of a 64-key sequence
