@@ -301,6 +301,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
     if (m0 >= M) return;
     const int32_t E = ui.keys_ok ? ui.kv_end : 0;
     const int32_t Hkv = p.kv_heads;
+    // A unit whose rows fit one tile has its keys read by one work group per
+    // kv head: they stream past the caches even when other units' tiles share
+    // theirs (column-store step 315-318 -> 311-313 us).
+    const bool own_keys = M <= BM;
 
     // The union of this tile's rows' visible ranges, cut into S parts.
     const int32_t pad = ui.pad;
@@ -445,8 +449,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
                 }
                 const uint8_t* kb = uniform_ptr(Kg + a);
                 const uint8_t* vb = uniform_ptr(Vg + a);
-                dma16s<STREAM>(issue_off[m], kb, (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024)));
-                dma16s<STREAM>(issue_off[m], vb, (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024)));
+                const uint32_t km = (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024));
+                const uint32_t vm = (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024));
+                if (STREAM || own_keys) {
+                    dma16s<true>(issue_off[m], kb, km);
+                    dma16s<true>(issue_off[m], vb, vm);
+                } else {
+                    dma16s<false>(issue_off[m], kb, km);
+                    dma16s<false>(issue_off[m], vb, vm);
+                }
             }
             return;
         }
@@ -819,7 +830,8 @@ static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
     // group only, so the chunks stream past the caches (long-context decode
     // with a group of 8: 364 -> 338 us; draft verify 470 -> 460 us).  With
     // several row tiles, the tiles of a unit read the same keys and the cached
-    // policy keeps them (the column-store step ran 3 % slower streamed).
+    // policy keeps them (the column-store step ran 3 % slower streamed); the
+    // kernel still streams the keys of units whose rows fit one tile.
     if constexpr (D == 128 || D == 256) {
         if (few_rows(D, (int64_t)p.max_seqlen_q * p.group)) {
             if (p.mfma_tiles != 1) return hipErrorInvalidValue;     // one tile holds every row
