@@ -490,8 +490,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int m = 0; m < IPW; ++m) {
             const int I = wave + NW * m;
-            dma16<STREAM>(ks[m], (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024)));
-            dma16<STREAM>(vs[m], (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024)));
+            const uint32_t km = (uint32_t)__builtin_amdgcn_readfirstlane((int)(kdst + I * 1024));
+            const uint32_t vm = (uint32_t)__builtin_amdgcn_readfirstlane((int)(vdst + I * 1024));
+            if (STREAM || own_keys) {
+                dma16<true>(ks[m], km);
+                dma16<true>(vs[m], vm);
+            } else {
+                dma16<false>(ks[m], km);
+                dma16<false>(vs[m], vm);
+            }
         }
     };
     // Stage the block ids of [blk, blk + kIdWindow) (paged): every thread calls it.
