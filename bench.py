@@ -628,7 +628,7 @@ def main():
                     help="plain launches instead of graph replays (for per-dispatch counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "one GPU only: the benchmark runs the single-GPU hot path, so --gpus must be 1"}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
