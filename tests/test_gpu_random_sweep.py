@@ -1,5 +1,6 @@
 """GPU parity over seeded random call shapes: head_dim 64/128/256, GQA groups
-1..16, bf16 and fp32, paged varlen (several sequences) and column-store calls,
+1..16, bf16 and fp32, paged varlen (2..16 sequences, up to 9000 keys and 100
+query rows in the wide set) and column-store calls,
 causal or not, windows, left-padding bounds and split counts drawn per case.
 Each case picks its own kernels through the library's routing (vector path,
 matrix-core shapes, fp32 row mode) and is compared, every output element,
@@ -17,6 +18,7 @@ from helpers import check_close, oracle_column, oracle_paged
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 N_CASES = 40
+N_WIDE = 60
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -26,22 +28,25 @@ def gpu():
     pkv.lib()
 
 
-def _draw(case: int) -> dict:
-    r = np.random.default_rng(5000 + case)
+def _draw(case: int, wide: bool = False) -> dict:
+    """Small shapes, or (wide) up to 16 units of up to 9000 keys and 100 query rows."""
+    r = np.random.default_rng((15000 if wide else 5000) + case)
     D = int(r.choice([64, 128, 256]))
     fp32 = bool(r.random() < 0.25)
     groups = [1, 2, 4, 8] if fp32 else [1, 2, 4, 8, 16]
     G = int(r.choice(groups))
     hkv = int(r.choice([1, 2, 4, 8]))
-    n = int(r.integers(2, 7))                          # sequences or segments (never one)
-    lq_max = int(r.choice([1, 1, 4, 16, 40]))
+    n = int(r.integers(2, 17 if wide else 7))         # sequences or segments (never one)
+    lq_max = int(r.choice([1, 1, 4, 16, 40, 100] if wide else [1, 1, 4, 16, 40]))
     q_lens = [int(x) for x in r.integers(1, lq_max + 1, size=n)]
-    lengths = [int(x) for x in r.integers(0, 1500, size=n)]
+    lengths = [int(x) for x in r.integers(0, 9000 if wide else 1500, size=n)]
     lengths = [max(E, L) for E, L in zip(lengths, q_lens)]
     return dict(D=D, dtype=torch.float32 if fp32 else torch.bfloat16, G=G, hkv=hkv, n=n, q_lens=q_lens,
                 lengths=lengths, causal=bool(r.random() < 0.7), window=int(r.choice([0, 0, 100, 700])),
                 splits=int(r.choice([0, 0, 1, 3, 7])), column=bool(r.random() < 0.35),
-                pad=bool(r.random() < 0.3), wrap=int(r.choice([0, 2500])), seed=6000 + 17 * case)
+                pad=bool(r.random() < 0.3), wrap=int(r.choice([0, 2500])),
+                rows=4096 if wide else 2048, cols=16 if wide else 8,
+                seed=(16000 if wide else 6000) + 17 * case)
 
 
 def _pads(c: dict, ends):
@@ -55,7 +60,15 @@ def _pads(c: dict, ends):
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_random_call_shape(case):
-    c = _draw(case)
+    _run(_draw(case), case)
+
+
+@pytest.mark.parametrize("case", range(N_WIDE))
+def test_random_call_shape_wide(case):
+    _run(_draw(case, wide=True), case)
+
+
+def _run(c: dict, case: int):
     name = "f32" if c["dtype"] == torch.float32 else "bf16"
     what = f"case {case}: {c}"
     hq = c["G"] * c["hkv"]
@@ -63,9 +76,9 @@ def test_random_call_shape(case):
         # A window lets a segment's keys run past the ring (rows >= window +
         # max_seqlen_q - 1 keeps every visible key stored); without one the
         # ring holds every key, E <= rows.
-        rows = 2048
+        rows = c["rows"]
         ends = [E + c["wrap"] if c["window"] > 0 else min(E, rows) for E in c["lengths"]]
-        inp = workloads.column_inputs(seed=c["seed"], rows=rows, cols=8, q_lens=c["q_lens"], kv_ends=ends,
+        inp = workloads.column_inputs(seed=c["seed"], rows=rows, cols=c["cols"], q_lens=c["q_lens"], kv_ends=ends,
                                       total_q=sum(c["q_lens"]) + 13, q_heads=hq, kv_heads=c["hkv"],
                                       head_dim=c["D"], dtype=c["dtype"], causal=c["causal"], window=c["window"],
                                       device=DEV)
